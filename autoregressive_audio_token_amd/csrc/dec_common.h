@@ -1,0 +1,99 @@
+// Shared device helpers for the decode-step kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dec {
+
+constexpr int kWave = 64;
+
+// ---- cross-lane moves (DPP within 16-lane rows, ds_swizzle/bpermute beyond) -------
+
+// DPP control codes (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowRor8 = 0x128;     // row_ror:8  == lane ^ 8 inside a 16-lane row
+constexpr int kDppRowMirror = 0x140;   // lane 15 - i inside a 16-lane row
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i inside an 8-lane half row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8 or 16); every lane of a group gets the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (G == 16) v += dpp_f32<kDppRowMirror>(v);
+  return v;
+}
+
+// Butterfly across lanes that differ in bit positions [log2(FROM), 6): combines the
+// values held by lanes lane ^ FROM, lane ^ 2*FROM, ... (all lanes end with the result).
+template <int FROM>
+__device__ __forceinline__ float xor_max_from(float v) {
+  if constexpr (FROM <= 8) v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
+  if constexpr (FROM <= 16) v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+template <int FROM>
+__device__ __forceinline__ float xor_sum_from(float v) {
+  if constexpr (FROM <= 8) v += dpp_f32<kDppRowRor8>(v);
+  if constexpr (FROM <= 16) v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+  return xor_max_from<16>(v);
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele, fixed order).
+__device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    float y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_exclusive_sum_int(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
+// ---- element decoding ------------------------------------------------------------
+
+// bfloat16 pair packed in a 32-bit word (little endian: element 2i in the low half).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+// ---- order-preserving key for float32 (host and device) ---------------------------
+// Monotone: a < b implies key(a) < key(b); -0 is folded onto +0 so equal values tie.
+__host__ __device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dec

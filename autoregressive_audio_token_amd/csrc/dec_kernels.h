@@ -1,0 +1,72 @@
+// Kernel parameter blocks and launchers shared by the kernel sources and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dec {
+
+// ---- attention (split-K flash-decode over the valid prefix) ----------------------
+
+constexpr int kAttnWaves = 4;                       // waves per workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnKeysPerWaveTile = 64;            // keys one wave loads per tile
+#ifndef DEC_ATTN_TILES
+#define DEC_ATTN_TILES 1
+#endif
+constexpr int kAttnTiles = DEC_ATTN_TILES;          // tiles per wave per chunk
+constexpr int kAttnChunk = kAttnWaves * kAttnKeysPerWaveTile * kAttnTiles;
+constexpr int kAttnPartStride = 68;                 // floats per partial: m, l, pad, pad, acc[64]
+constexpr int kAttnHeadDim = 64;
+constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
+
+// One attention problem ("segment"): self-attention or cross-attention of a step.
+struct AttnSeg {
+  const void* q;          // [NL, B, H, 64]
+  const void* k;          // [NL, B, H, L_cap, 64]
+  const void* v;          // [NL, B, H, L_cap, 64]
+  const int32_t* len;     // [B] valid slots
+  float* out;             // [NL, B, H, 64]
+  float* part;            // [NL*B*H, nck_cap, kAttnPartStride] split-K partials (or null)
+  int32_t* ticket;        // [NL*B*H] arrival counters, zero between calls (or null)
+  int L_cap;
+  int nck_cap;            // ceil(L_cap / kAttnChunk)
+};
+
+struct AttnParams {
+  AttnSeg seg[2];
+  int nseg;
+  int NL, B, H;
+  float qscale;           // scale * log2(e): scores are formed in base 2
+};
+
+// Upper bound on the work items of a launch (every sequence at full capacity).
+long long attn_items_cap(const AttnParams& p);
+// Enqueue the attention kernel; `blocks` <= 0 picks the occupancy-sized grid.
+hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream);
+
+// ---- sampler ---------------------------------------------------------------------
+
+constexpr int kSampWaves = 4;                       // rows (one per wave) per workgroup
+constexpr int kSampMaxVocab = 4096;
+
+struct SampleParams {
+  const float* logits;
+  const float* temperature;
+  const float* uniforms;
+  const int32_t* step;
+  int32_t* tokens;
+  int32_t* topk_idx;
+  float* topk_prob;
+  int B, n_cb, V_valid, V_stride, top_k, fill;
+};
+
+hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
+
+// ---- small utility kernels ------------------------------------------------------------
+
+hipError_t fill_zero_launch(void* ptr, size_t bytes, hipStream_t stream);
+hipError_t advance_launch(int32_t* len, int32_t* step, int B, hipStream_t stream);
+
+}  // namespace dec

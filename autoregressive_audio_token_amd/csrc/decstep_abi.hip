@@ -1,0 +1,272 @@
+// The C ABI (include/decstep.h): host-side validation, workspace layout, launches
+// and graph helpers.  No entry point allocates, synchronises or reads device data.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/decstep.h"
+#include "dec_common.h"
+#include "dec_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = static_cast<int>(e);
+  return DEC_E_HIP;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Workspace of one attention segment: arrival counters, then split-K partials.
+// Segments whose capacity fits one chunk need neither.
+struct SegLayout {
+  size_t ticket_off = 0, part_off = 0, bytes = 0;
+  int nck_cap = 1;
+};
+
+SegLayout seg_layout(int NL, int B, int H, int L_cap) {
+  SegLayout s;
+  if (L_cap <= 0) return s;
+  s.nck_cap = (L_cap + dec::kAttnChunk - 1) / dec::kAttnChunk;
+  if (s.nck_cap <= 1) return s;
+  const size_t nseq = (size_t)NL * B * H;
+  s.ticket_off = 0;
+  s.part_off = align_up(nseq * sizeof(int32_t), 256);
+  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
+  return s;
+}
+
+bool sizes_ok(int NL, int B, int H, int L_cap) {
+  if (NL < 1 || B < 1 || H < 1 || L_cap < 1) return false;
+  const long long nseq = (long long)NL * B * H;
+  if (nseq > (1LL << 30)) return false;
+  const long long elems = nseq * L_cap * dec::kAttnHeadDim;
+  return elems < (1LL << 46);
+}
+
+// Optional grid override for tuning and for grid-independence tests.
+int grid_override() {
+  const char* s = getenv("DECSTEP_ATTN_BLOCKS");
+  if (s == nullptr) return 0;
+  const int v = atoi(s);
+  return v > 0 ? v : 0;
+}
+
+struct SegArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* len;
+  float* out;
+  int L_cap;
+};
+
+int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int dtype,
+                float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  for (int s = 0; s < nseg; ++s) {
+    if (!segs[s].q || !segs[s].k || !segs[s].v || !segs[s].len || !segs[s].out) return DEC_E_NULL;
+  }
+  if (dtype != DEC_BF16 && dtype != DEC_F32) return DEC_E_DTYPE;
+  for (int s = 0; s < nseg; ++s) {
+    if (!sizes_ok(NL, B, H, segs[s].L_cap)) return DEC_E_SHAPE;
+  }
+  if (hd != dec::kAttnHeadDim) return DEC_E_UNSUPPORTED;
+  if (nseg * B > dec::kAttnMaxGroups) return DEC_E_UNSUPPORTED;
+  for (int s = 0; s < nseg; ++s) {
+    if (!aligned(segs[s].q, 16) || !aligned(segs[s].k, 16) || !aligned(segs[s].v, 16) ||
+        !aligned(segs[s].len, 4) || !aligned(segs[s].out, 4))
+      return DEC_E_ALIGN;
+  }
+  size_t need = 0;
+  SegLayout lay[2];
+  for (int s = 0; s < nseg; ++s) {
+    lay[s] = seg_layout(NL, B, H, segs[s].L_cap);
+    need += lay[s].bytes;
+  }
+  if (need > 0) {
+    if (ws == nullptr) return DEC_E_NULL;
+    if (!aligned(ws, 16)) return DEC_E_ALIGN;
+    if (ws_bytes < need) return DEC_E_WORKSPACE;
+  }
+
+  dec::AttnParams p{};
+  p.nseg = nseg;
+  p.NL = NL;
+  p.B = B;
+  p.H = H;
+  p.qscale = scale * 1.4426950408889634f;  // log2(e)
+  size_t off = 0;
+  for (int s = 0; s < nseg; ++s) {
+    dec::AttnSeg& g = p.seg[s];
+    g.q = segs[s].q;
+    g.k = segs[s].k;
+    g.v = segs[s].v;
+    g.len = segs[s].len;
+    g.out = segs[s].out;
+    g.L_cap = segs[s].L_cap;
+    g.nck_cap = lay[s].nck_cap;
+    if (lay[s].bytes > 0) {
+      char* base = static_cast<char*>(ws) + off;
+      g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
+      g.part = reinterpret_cast<float*>(base + lay[s].part_off);
+    }
+    off += lay[s].bytes;
+  }
+  if (nseg == 1) p.seg[1] = p.seg[0];
+  const hipError_t e = dec::attn_launch(p, dtype, grid_override(), stream);
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dec_attn_chunk_keys(void) { return dec::kAttnChunk; }
+
+size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_self,
+                                int L_cap_cross) {
+  if (hd != dec::kAttnHeadDim || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 0 ||
+      L_cap_cross < 0)
+    return 0;
+  return seg_layout(n_layers, B, H, L_cap_self).bytes +
+         seg_layout(n_layers, B, H, L_cap_cross).bytes;
+}
+
+int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {
+  if (ws_bytes == 0) return DEC_OK;
+  if (workspace == nullptr) return DEC_E_NULL;
+  if (!aligned(workspace, 16)) return DEC_E_ALIGN;
+  const hipError_t e = dec::fill_zero_launch(workspace, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_attn_self(const void* q, const void* k, const void* v, const int32_t* len, float* out,
+                  int n_layers, int B, int H, int L_cap, int hd, int dtype, float scale,
+                  void* workspace, size_t ws_bytes, dec_stream_t stream) {
+  const SegArgs s{q, k, v, len, out, L_cap};
+  return attn_common(&s, 1, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_cross(const void* q, const void* k, const void* v, const int32_t* enc_len,
+                   float* out, int n_layers, int B, int H, int L_cap, int hd, int dtype,
+                   float scale, void* workspace, size_t ws_bytes, dec_stream_t stream) {
+  const SegArgs s{q, k, v, enc_len, out, L_cap};
+  return attn_common(&s, 1, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_step(const void* q_self, const void* k_self, const void* v_self, const int32_t* len,
+                  int L_cap_self, float* out_self, const void* q_cross, const void* k_cross,
+                  const void* v_cross, const int32_t* enc_len, int L_cap_cross, float* out_cross,
+                  int n_layers, int B, int H, int hd, int dtype, float scale, void* workspace,
+                  size_t ws_bytes, dec_stream_t stream) {
+  const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
+                        {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_sample_topk(const float* logits, int B, int n_cb, int V_valid, int V_stride,
+                    const float* temperature, int top_k, const float* uniforms,
+                    const int32_t* step, int32_t fill_token, int32_t* tokens, int32_t* topk_idx,
+                    float* topk_prob, dec_stream_t stream) {
+  if (!logits || !temperature || !uniforms || !tokens) return DEC_E_NULL;
+  if (B < 1 || n_cb < 1 || V_valid < 1 || V_stride < V_valid) return DEC_E_SHAPE;
+  if ((long long)B * n_cb > (1LL << 30) || (long long)B * n_cb * V_stride > (1LL << 46))
+    return DEC_E_SHAPE;
+  if (top_k < 1 || top_k > 64) return DEC_E_SHAPE;
+  if (V_valid > dec::kSampMaxVocab) return DEC_E_UNSUPPORTED;
+  if (!aligned(logits, 4) || !aligned(temperature, 4) || !aligned(uniforms, 4) ||
+      !aligned(step, 4) || !aligned(tokens, 4) || !aligned(topk_idx, 4) || !aligned(topk_prob, 4))
+    return DEC_E_ALIGN;
+  dec::SampleParams p{};
+  p.logits = logits;
+  p.temperature = temperature;
+  p.uniforms = uniforms;
+  p.step = step;
+  p.tokens = tokens;
+  p.topk_idx = topk_idx;
+  p.topk_prob = topk_prob;
+  p.B = B;
+  p.n_cb = n_cb;
+  p.V_valid = V_valid;
+  p.V_stride = V_stride;
+  p.top_k = top_k;
+  p.fill = fill_token;
+  const hipError_t e = dec::sample_launch(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream) {
+  if (B < 1) return DEC_E_SHAPE;
+  if (len == nullptr && step == nullptr) return DEC_E_NULL;
+  if (!aligned(len, 4) || !aligned(step, 4)) return DEC_E_ALIGN;
+  const hipError_t e = dec::advance_launch(len, step, B, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_graph_begin(dec_stream_t stream) {
+  if (stream == nullptr) return DEC_E_NULL;
+  const hipError_t e =
+      hipStreamBeginCapture(reinterpret_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal);
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_graph_end(dec_stream_t stream, void** exec) {
+  if (stream == nullptr || exec == nullptr) return DEC_E_NULL;
+  *exec = nullptr;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(reinterpret_cast<hipStream_t>(stream), &graph);
+  if (e != hipSuccess) return hip_fail(e);
+  hipGraphExec_t ge = nullptr;
+  e = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+  const hipError_t e2 = hipGraphDestroy(graph);
+  if (e != hipSuccess) return hip_fail(e);
+  if (e2 != hipSuccess) {
+    (void)hipGraphExecDestroy(ge);
+    return hip_fail(e2);
+  }
+  *exec = ge;
+  return DEC_OK;
+}
+
+int dec_graph_launch(void* exec, dec_stream_t stream) {
+  if (exec == nullptr) return DEC_E_NULL;
+  const hipError_t e =
+      hipGraphLaunch(static_cast<hipGraphExec_t>(exec), reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_graph_destroy(void* exec) {
+  if (exec == nullptr) return DEC_E_NULL;
+  const hipError_t e = hipGraphExecDestroy(static_cast<hipGraphExec_t>(exec));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_last_hip_error(void) { return g_last_hip; }
+
+const char* dec_strerror(int status) {
+  switch (status) {
+    case DEC_OK: return "DEC_OK: success";
+    case DEC_E_NULL: return "DEC_E_NULL: a required pointer is NULL";
+    case DEC_E_SHAPE: return "DEC_E_SHAPE: a size is out of range or sizes disagree";
+    case DEC_E_DTYPE: return "DEC_E_DTYPE: unknown dtype code";
+    case DEC_E_WORKSPACE: return "DEC_E_WORKSPACE: workspace too small";
+    case DEC_E_UNSUPPORTED: return "DEC_E_UNSUPPORTED: case not implemented (e.g. head_dim != 64)";
+    case DEC_E_HIP: return "DEC_E_HIP: a HIP runtime call failed (see dec_last_hip_error)";
+    case DEC_E_ALIGN: return "DEC_E_ALIGN: pointer not aligned as required";
+    default: return "unknown dec_status";
+  }
+}
+
+void dec_order_keys_host(const float* x, uint32_t* keys, size_t n) {
+  if (x == nullptr || keys == nullptr) return;
+  for (size_t i = 0; i < n; ++i) keys[i] = dec::order_key(x[i]);
+}
+
+}  // extern "C"

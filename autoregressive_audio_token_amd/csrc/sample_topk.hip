@@ -1,0 +1,193 @@
+// Fused temperature / top-k / softmax / inverse-CDF sampling with the codebook
+// delay mask, one wavefront per (sequence, codebook) row (gfx950).
+//
+// "Optimized Parler TTS", "Future work", item 2: sampling was more than ten
+// kernels (temperature, top-k, softmax) with global-memory round trips between
+// them.  Here one kernel reads each row of logits once and writes the token.
+// "Analysis and improvements": logits exist for the last position only (one
+// row per codebook) and the vocabulary is padded to a multiple of 8 -- the
+// padding columns are never read.  Random numbers arrive as per-row uniforms,
+// so nothing waits on the host.  "A rough architecture of Parler TTS": 9
+// codebooks per step under a delay pattern; codebook c emits the fill token
+// until the sequence has taken c steps.
+//
+// Per row (64 lanes):
+//   1. Stage the row through LDS so each lane owns a CONTIGUOUS run of VPL
+//      vocabulary entries (vocabulary order == lane order, then slot order).
+//   2. Map values to order-preserving uint32 keys and find the kk-th largest
+//      key by MSB-first bisection; each step counts keys >= candidate with
+//      wave ballots (exact, integer only).
+//   3. Keep keys above the threshold plus the lowest-index entries equal to it
+//      (a wave prefix count ranks ties in vocabulary order); compact the kept
+//      entries through LDS so lane t holds the t-th kept entry in ascending
+//      vocabulary order (kk <= 64).
+//   4. e_t = exp((x_t - max) / T); wave inclusive scan; C_t = S_t / S_last;
+//      the token is the first kept entry with u < C_t.  T <= 0: greedy.
+#include "dec_common.h"
+#include "dec_kernels.h"
+
+namespace dec {
+
+template <int VPL>
+__global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
+  constexpr int STR = VPL | 1;  // odd LDS stride: the contiguous-run reads do not conflict
+  extern __shared__ float s_buf[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int rows = p.B * p.n_cb;
+  const int row = blockIdx.x * kSampWaves + wave;
+  const bool active = row < rows;  // uniform per wave; inactive waves still reach barriers
+
+  float* buf = s_buf + wave * (kWave * STR + 2 * kWave);
+  float* cval = buf + kWave * STR;
+  int* cidx = reinterpret_cast<int*>(cval + kWave);
+
+  if (active) {
+    const float* x = p.logits + (size_t)row * p.V_stride;
+    for (int i = lane; i < p.V_valid; i += kWave) {
+      const int o = i / VPL;
+      buf[o * STR + (i - o * VPL)] = x[i];
+    }
+  }
+  __syncthreads();
+
+  const int kk = p.top_k < p.V_valid ? p.top_k : p.V_valid;
+  if (active) {
+    const int gbase = lane * VPL;
+    float v[VPL];
+    uint32_t key[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const bool ok = gbase + j < p.V_valid;
+      v[j] = ok ? buf[lane * STR + j] : 0.f;
+      key[j] = ok ? order_key(v[j]) : 0u;  // invalid slots: below every candidate
+    }
+    // threshold: the largest t with #(key >= t) >= kk, i.e. the kk-th largest key;
+    // stop early once exactly kk keys are >= t
+    uint32_t tau = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+      if (cnt >= kk) {
+        tau = cand;
+        if (cnt == kk) break;
+      }
+    }
+    int cnt_gt = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
+    const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
+    int my_eq = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) my_eq += (gbase + j < p.V_valid && key[j] == tau) ? 1 : 0;
+    int rank = wave_exclusive_sum_int(my_eq, lane);
+    bool kept[VPL];
+    int my_kept = 0;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const bool eq = gbase + j < p.V_valid && key[j] == tau;
+      kept[j] = key[j] > tau || (eq && rank < need);
+      rank += eq ? 1 : 0;
+      my_kept += kept[j] ? 1 : 0;
+    }
+    int off = wave_exclusive_sum_int(my_kept, lane);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      if (kept[j]) {
+        cval[off] = v[j];
+        cidx[off] = gbase + j;
+        ++off;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (active) {
+    const bool act = lane < kk;
+    const float xv = act ? cval[lane] : -INFINITY;
+    const int xi = act ? cidx[lane] : -1;
+    const int b = row / p.n_cb;
+    const int c = row - b * p.n_cb;
+    const float T = p.temperature[b];
+    const float m = wave_max(xv);
+    int sel;
+    float prob;
+    if (T <= 0.f) {
+      const unsigned long long mk = __ballot(act && xv == m);
+      sel = mk ? __ffsll(mk) - 1 : 0;
+      prob = lane == sel ? 1.f : 0.f;
+    } else {
+      const float e = act ? expf((xv - m) / T) : 0.f;
+      const float S = wave_inclusive_sum(e, lane);
+      const float Z = __shfl(S, kk - 1);
+      const float C = S / Z;
+      const float u = p.uniforms[row];
+      const unsigned long long mk = __ballot(act && u < C);
+      sel = mk ? __ffsll(mk) - 1 : kk - 1;
+      prob = e / Z;
+    }
+    int token = __shfl(xi, sel);
+    if (p.step != nullptr && p.step[b] < c) token = p.fill;
+    if (lane == 0) p.tokens[row] = token;
+    if (lane < p.top_k) {
+      if (p.topk_idx != nullptr) p.topk_idx[(size_t)row * p.top_k + lane] = act ? xi : -1;
+      if (p.topk_prob != nullptr) p.topk_prob[(size_t)row * p.top_k + lane] = act ? prob : 0.f;
+    }
+  }
+}
+
+template <int VPL>
+static hipError_t sample_launch_vpl(const SampleParams& p, hipStream_t stream) {
+  constexpr int STR = VPL | 1;
+  const int rows = p.B * p.n_cb;
+  const int blocks = (rows + kSampWaves - 1) / kSampWaves;
+  const size_t lds = (size_t)kSampWaves * (kWave * STR + 2 * kWave) * sizeof(float);
+  hipLaunchKernelGGL(sample_topk_kernel<VPL>, dim3(blocks), dim3(kSampWaves * kWave), lds, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t sample_launch(const SampleParams& p, hipStream_t stream) {
+  const int need = (p.V_valid + kWave - 1) / kWave;  // entries per lane
+  if (need <= 4) return sample_launch_vpl<4>(p, stream);
+  if (need <= 8) return sample_launch_vpl<8>(p, stream);
+  if (need <= 16) return sample_launch_vpl<16>(p, stream);
+  if (need <= 18) return sample_launch_vpl<18>(p, stream);
+  if (need <= 32) return sample_launch_vpl<32>(p, stream);
+  return sample_launch_vpl<64>(p, stream);
+}
+
+// ---- utilities ------------------------------------------------------------------------
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t fill_zero_launch(void* ptr, size_t bytes, hipStream_t stream) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ptr), n);
+  return hipGetLastError();
+}
+
+__global__ void advance_kernel(int32_t* len, int32_t* step, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    if (len != nullptr) len[b] += 1;
+    if (step != nullptr) step[b] += 1;
+  }
+}
+
+hipError_t advance_launch(int32_t* len, int32_t* step, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(advance_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, len, step, B);
+  return hipGetLastError();
+}
+
+}  // namespace dec

@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: self-attention over
+the valid prefix of the static cache and cross-attention over the description
+for all layers (one fused launch), then the fused top-k sampler over the 9
+codebooks.  Steps run as a captured hipGraph that chains one step per cache
+set; the R cache sets are distinct allocations so each step reads cold data
+(R x valid bytes exceeds the 256 MB Infinity Cache).
+
+Prints ONE JSON line: value = valid K/V bytes per step / time per step (GB/s).
+
+    python bench.py [--steps K] [--warmup W] [--workload long_description]
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "decode-step µs and achieved HBM GB/s (valid KV bytes) vs MI355X peak"
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="long_description")
+    ap.add_argument("--sets", type=int, default=0, help="cache sets (0: enough for >= 1 GiB)")
+    ap.add_argument("--kernel-launches", type=int, default=200,
+                    help="event-timed attention launches for the roofline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args(argv)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, as it stands, on whole decode steps of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attn as oattn, sampling as osamp
+    from workloads import configs, gen
+
+    s_len, c_len = gen.lengths(w)
+    q = {k: gen.queries(w, k) for k in ("self", "cross")}
+    lens = {"self": s_len, "cross": c_len}
+    rows = {}
+    for kind in ("self", "cross"):
+        for layer in range(w.n_layers):
+            for b in range(w.batch):
+                n = int(lens[kind][b])
+                rows[kind, layer, b] = (gen.kv_rows(w, kind, "k", layer, b, n),
+                                        gen.kv_rows(w, kind, "v", layer, b, n))
+    lg, u, T = gen.logits(w), gen.uniforms(w), gen.temperatures(w)
+    dec16 = oattn.bf16_bits_to_f64 if w.dtype == "bf16" else (lambda x: x.astype(np.float64))
+
+    def one_step():
+        for kind in ("self", "cross"):
+            for layer in range(w.n_layers):
+                for b in range(w.batch):
+                    K, V = rows[kind, layer, b]
+                    n = int(lens[kind][b])
+                    for h in range(w.heads):
+                        oattn.attend_one(dec16(q[kind][layer, b, h]), dec16(K[h]), dec16(V[h]),
+                                         n, w.scale)
+        osamp.sample(lg, w.vocab_valid, T, w.top_k, u, None, w.fill_token)
+
+    with threadpool_limits(1):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            one_step()
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    valid = configs.valid_kv_bytes(w, s_len, c_len)
+    return {"value": round(valid * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} whole decode steps of {w.name} (all layers, self+cross "
+                      f"attention over the valid prefixes, then the sampler), float64 NumPy, "
+                      f"one thread",
+            "us_per_step": round(el / steps * 1e6, 1),
+            "host_cpu": platform.processor() or platform.machine(),
+            "host_cores_visible": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    a = parse(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has "
+              "no multi-GPU path: every GPU box here has a single MI355X.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import autoregressive_audio_token_amd as dec
+    from workloads import configs, gen, device as wdev
+
+    w = configs.BY_NAME[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s_len, c_len = gen.lengths(w)
+    valid = configs.valid_kv_bytes(w, s_len, c_len)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    log(f"workload {w.name}: staging inputs")
+    d = wdev.step_inputs(w, dev)
+    R = a.sets if a.sets > 0 else max(2, math.ceil((1 << 30) / valid))
+    big = ("k_self", "v_self", "k_cross", "v_cross")
+    sets = [{k: d[k] for k in big}]
+    for _ in range(R - 1):
+        sets.append({k: torch.empty_like(d[k]).copy_(d[k]) for k in big})
+    static_bytes = sum(d[k].numel() * d[k].element_size() for k in big)
+    code = dec.DEC_BF16 if w.dtype == "bf16" else dec.DEC_F32
+    nb = dec.dec_attn_workspace_bytes(w.n_layers, w.batch, w.heads, w.head_dim, w.self_cap,
+                                      w.cross_cap)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    o_s = torch.empty((w.n_layers, w.batch, w.heads, w.head_dim), dtype=torch.float32,
+                      device=dev)
+    o_c = torch.empty_like(o_s)
+    tok = torch.empty((w.batch, w.n_codebooks), dtype=torch.int32, device=dev)
+    step_t = d["step"] if w.delay else None
+    stream = torch.cuda.Stream(device=dev)
+
+    def attn(st, s):
+        dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], d["len"], w.self_cap, o_s,
+                          d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
+                          o_c, w.n_layers, w.batch, w.heads, w.head_dim, code, w.scale, ws, nb,
+                          s)
+
+    def sample(s):
+        dec.dec_sample_topk(d["logits"], w.batch, w.n_codebooks, w.vocab_valid, w.vocab_stride,
+                            d["temperature"], w.top_k, d["uniforms"], step_t, w.fill_token, tok,
+                            None, None, s)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        dec.dec_attn_workspace_init(ws, nb, stream)
+        for st in sets:                  # eager warm-up of every set
+            attn(st, stream)
+            sample(stream)
+        stream.synchronize()
+        dec.dec_graph_begin(stream)
+        for st in sets:
+            attn(st, stream)
+            sample(stream)
+        graph = dec.dec_graph_end(stream)
+
+    log(f"{R} cache sets captured; timing")
+    launches = max(1, math.ceil(a.steps / R))
+    steps = launches * R
+    warm = max(1, math.ceil(a.warmup / R))
+    for _ in range(warm):
+        dec.dec_graph_launch(graph, stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(launches):
+        dec.dec_graph_launch(graph, stream)
+    e1.record(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    out_ok = bool(torch.isfinite(o_s).all().item() and torch.isfinite(o_c).all().item())
+    tok_h = tok.cpu().numpy()
+    tok_ok = bool(np.all((tok_h >= 0) & (tok_h < w.vocab_valid) | (tok_h == w.fill_token)))
+
+    # roofline leg: the attention kernel alone, each launch bracketed by its own events
+    n_k = max(R, a.kernel_launches)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_k)]
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        l0.record(stream)
+        for i in range(n_k):
+            evs[i][0].record(stream)
+            attn(sets[i % R], stream)
+            evs[i][1].record(stream)
+        l1.record(stream)
+    stream.synchronize()
+    per = sorted(s.elapsed_time(e) * 1e3 for s, e in evs)        # microseconds
+    k_us = sum(per) / len(per)
+    k_loop_us = l0.elapsed_time(l1) * 1e3 / n_k
+    achieved = valid / (k_us * 1e-6) / 1e9
+    dec.dec_graph_destroy(graph)
+
+    result = {
+        "metric": METRIC,
+        "value": round(valid / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm * R,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "n_layers": w.n_layers, "batch": w.batch, "heads": w.heads,
+            "head_dim": w.head_dim, "self_len": [int(x) for x in s_len][:4],
+            "self_cap": w.self_cap, "cross_len": [int(x) for x in c_len][:4],
+            "cross_cap": w.cross_cap, "codebooks": w.n_codebooks, "vocab": w.vocab_valid,
+            "vocab_stride": w.vocab_stride, "top_k": w.top_k, "accumulate": "f32",
+            "valid_kv_bytes_per_step": valid, "cache_sets": R,
+            "static_cache_bytes_per_set": static_bytes,
+            "schedule": "hipGraph of R steps; step = dec_attn_step (self+cross, all layers, "
+                        "one launch) + dec_sample_topk",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "attn_decode_kernel (dec_attn_step)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(k_us, 3), "median_launch_us": round(per[len(per) // 2], 3),
+            "loop_avg_us": round(k_loop_us, 3), "launches": n_k,
+            "algorithmic_bytes_per_launch": valid,
+        },
+        "checks": {"outputs_finite": out_ok, "tokens_in_range": tok_ok},
+        "host_wall_s": round(wall, 4),
+    }
+    log(f"{ms_per_step * 1e3:.2f} us/step; attention launch {k_us:.2f} us")
+    if not a.no_cpu_baseline:
+        log("timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0 if (out_ok and tok_ok) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

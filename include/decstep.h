@@ -1,0 +1,172 @@
+/*
+ * decstep.h -- C ABI of the decode-step hot path of a Parler-TTS-style
+ * multi-codebook audio-token decoder, for AMD Instinct MI355X (gfx950).
+ *
+ * Source: the "Optimized Parler TTS" page.  One decode step of its decoder
+ * (a MusicGen-style autoregressive decoder, "A rough architecture of Parler
+ * TTS") does, per layer, single-token causal self-attention over a static KV
+ * cache and cross-attention over the encoded description, and ends by
+ * sampling one token for each of the 9 DAC codebooks.  "Analysis and
+ * improvements" keeps both caches static and preallocated so that a whole
+ * step can be captured as one graph, and samples without a GPU/CPU
+ * synchronisation; "Future work" asks for paged attention against the cost of
+ * moving the whole static cache, and for one fused sampling kernel in place of
+ * the ten-plus temperature / top-k / softmax kernels.  This library reads only
+ * the valid prefix of each static cache and samples in one kernel.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     every buffer; the library never allocates, frees, synchronises or reads
+ *     device data on the host, so every call is legal inside hip stream
+ *     capture.  All work is enqueued on `stream` (a hipStream_t, may be NULL
+ *     for the default stream) and is asynchronous.
+ *   - Layouts are row-major and contiguous.  bf16 tensors hold IEEE bfloat16
+ *     bit patterns.  q, k, v and the workspace must be 16-byte aligned, every
+ *     other device pointer 4-byte aligned.
+ *   - The return value is a dec_status.  Problems visible on the host are
+ *     reported before anything is enqueued (nothing is launched, no HIP call
+ *     is made).  DEC_E_HIP means a HIP call failed; dec_last_hip_error()
+ *     returns its hipError_t (per calling thread).
+ *   - Values that live on the device cannot be checked on the host; they have
+ *     defined results instead (stated per function).
+ */
+#ifndef DECSTEP_H
+#define DECSTEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dec_stream_t;   /* the same type as hipStream_t */
+
+enum dec_dtype { DEC_BF16 = 0, DEC_F32 = 1 };
+
+enum dec_status {
+  DEC_OK = 0,
+  DEC_E_NULL = 1,         /* a required pointer is NULL */
+  DEC_E_SHAPE = 2,        /* a size is out of range or sizes disagree */
+  DEC_E_DTYPE = 3,        /* unknown dtype code */
+  DEC_E_WORKSPACE = 4,    /* workspace smaller than dec_attn_workspace_bytes() */
+  DEC_E_UNSUPPORTED = 5,  /* a legal but unimplemented case (e.g. head_dim != 64) */
+  DEC_E_HIP = 6,          /* a HIP runtime call failed */
+  DEC_E_ALIGN = 7         /* a pointer is not aligned as required */
+};
+
+/* Keys per split-K chunk of the attention kernels: a sequence of n valid keys
+ * is split into max(1, ceil(n / chunk)) chunks whose partial softmax states
+ * are combined in chunk order.  The split depends on n only, never on the
+ * grid, so results are bitwise reproducible run to run. */
+int dec_attn_chunk_keys(void);
+
+/* Workspace bytes for attention over n_layers x B x H sequences with a self
+ * cache of L_cap_self slots and a cross cache of L_cap_cross slots (pass 0 for
+ * a cache that the call does not use).  One workspace sized for both serves
+ * dec_attn_self, dec_attn_cross and dec_attn_step.  Returns 0 on bad sizes. */
+size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,
+                                int L_cap_self, int L_cap_cross);
+
+/* Zero a workspace (a fill kernel, not a memset, so it may be captured).
+ * Required once after allocation; every attention call leaves the workspace's
+ * counters at zero again when it completes.  Calls that share one workspace
+ * must be ordered (same stream); concurrent use of one workspace races. */
+int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream);
+
+/* Single-token self-attention over the valid prefix of a static KV cache
+ * ("Analysis and improvements": static caches for causal attention; only the
+ * valid prefix is read, unlike the whole-cache transfer described there).
+ *
+ *   q    [n_layers, B, H, hd]          dtype
+ *   k, v [n_layers, B, H, L_cap, hd]   dtype; slots >= len[b] are never read
+ *   len  [B] int32, valid slots of sequence b INCLUDING the current token
+ *   out  [n_layers, B, H, hd] float32:
+ *          out = sum_j softmax_j(scale * <q, k_j>) v_j   over j < len[b]
+ *   hd must be 64; dtype is DEC_BF16 or DEC_F32; accumulation is float32.
+ * Device-side values: len[b] <= 0 gives an all-zero output row; len[b] >
+ * L_cap is read as L_cap.  n_layers > 1 means layer-stacked buffers served by
+ * one launch. */
+int dec_attn_self(const void* q, const void* k, const void* v, const int32_t* len,
+                  float* out, int n_layers, int B, int H, int L_cap, int hd, int dtype,
+                  float scale, void* workspace, size_t ws_bytes, dec_stream_t stream);
+
+/* Cross-attention over the encoded description ("A rough architecture of
+ * Parler TTS": the description states feed cross-attention in the decoder;
+ * "Analysis and improvements": the static cross-attention cache).  Same
+ * arguments as dec_attn_self with enc_len [B] (valid description states) in
+ * place of len and L_cap the description capacity. */
+int dec_attn_cross(const void* q, const void* k, const void* v, const int32_t* enc_len,
+                   float* out, int n_layers, int B, int H, int L_cap, int hd, int dtype,
+                   float scale, void* workspace, size_t ws_bytes, dec_stream_t stream);
+
+/* Self-attention and cross-attention of the same step in ONE launch: equal to
+ * dec_attn_self(q_self, ...) followed by dec_attn_cross(q_cross, ...), bit for
+ * bit.  workspace must hold dec_attn_workspace_bytes(n_layers, B, H, hd,
+ * L_cap_self, L_cap_cross) bytes. */
+int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
+                  const int32_t* len, int L_cap_self, float* out_self,
+                  const void* q_cross, const void* k_cross, const void* v_cross,
+                  const int32_t* enc_len, int L_cap_cross, float* out_cross,
+                  int n_layers, int B, int H, int hd, int dtype, float scale,
+                  void* workspace, size_t ws_bytes, dec_stream_t stream);
+
+/* Fused temperature / top-k / softmax / sampling of the next token of every
+ * codebook, with the codebook delay mask ("Future work", item 2: one kernel in
+ * place of the temperature, top-k and softmax kernels; "Analysis and
+ * improvements": logits of the last position only, vocabulary padded to a
+ * multiple of 8, sampling without a GPU/CPU synchronisation; "A rough
+ * architecture of Parler TTS": 9 codebooks under a delay pattern).
+ *
+ *   logits      [B, n_cb, V_stride] float32; only columns < V_valid are read
+ *   temperature [B] float32; T <= 0 selects greedy argmax
+ *   top_k       1..64 (a row keeps min(top_k, V_valid) entries)
+ *   uniforms    [B, n_cb] float32 in [0, 1)
+ *   step        [B] int32 steps already taken, or NULL for no delay mask
+ *   tokens      [B, n_cb] int32 out
+ *   topk_idx    [B, n_cb, top_k] int32 out or NULL: the kept vocabulary indices
+ *               in ascending order, -1 past min(top_k, V_valid)
+ *   topk_prob   [B, n_cb, top_k] float32 out or NULL: their probabilities
+ *               (one-hot on the chosen entry when T <= 0), 0 past the end
+ * Per row: keep the min(top_k, V_valid) largest logits (equal values: the
+ * lower index first); p_i = exp((x_i - max) / T) normalised over the kept set;
+ * walking the kept set in ascending vocabulary order, the token is the first
+ * index whose running sum of p exceeds u (the last kept index if none does).
+ * If step != NULL and step[b] < c, codebook c emits fill_token instead.
+ * Device-side values: non-finite logits or temperatures are outside the
+ * contract but still yield an index in [0, V_valid) or fill_token. */
+int dec_sample_topk(const float* logits, int B, int n_cb, int V_valid, int V_stride,
+                    const float* temperature, int top_k, const float* uniforms,
+                    const int32_t* step, int32_t fill_token, int32_t* tokens,
+                    int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
+
+/* Advance device-resident decode state by one step inside a captured graph:
+ * len[b] += 1 (if len != NULL) and step[b] += 1 (if step != NULL) for b < B. */
+int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);
+
+/* Graph capture of a whole decode step ("Analysis and improvements": the step
+ * is captured once and replayed with a single launch).  begin/end bracket
+ * ordinary dec_* calls on a non-default stream; end returns an executable
+ * graph in *exec (an opaque hipGraphExec_t). */
+int dec_graph_begin(dec_stream_t stream);
+int dec_graph_end(dec_stream_t stream, void** exec);
+int dec_graph_launch(void* exec, dec_stream_t stream);
+int dec_graph_destroy(void* exec);
+
+/* The hipError_t of the last failed HIP call made by this thread. */
+int dec_last_hip_error(void);
+
+/* A static string naming a dec_status code. */
+const char* dec_strerror(int status);
+
+/* Host-only helper: the order-preserving float -> uint32 key map that the
+ * sampler's top-k selection uses (a < b  =>  key(a) < key(b); -0 and +0 map
+ * alike).  keys[i] = key(x[i]) for i < n.  Both pointers are HOST pointers.
+ * Exposed so the map can be checked exhaustively on the CPU. */
+void dec_order_keys_host(const float* x, uint32_t* keys, size_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECSTEP_H */

@@ -1,0 +1,176 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects
+bad arguments on the host before any HIP call (fake device addresses are safe here
+because every case below fails validation first).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import autoregressive_audio_token_amd as dec
+from autoregressive_audio_token_amd import decstep as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decstep.h")
+A = 0x10000          # a fake, 16-byte aligned "device address" (never dereferenced)
+
+# These cases hand fake addresses to the library; they are host-logic tests and run
+# only where no GPU is visible, so a case that slipped past validation could never
+# reach a device.
+_no_gpu = pytest.mark.skipif(os.environ.get("DECSTEP_FAKE_PTR_TESTS") != "1" and
+                             __import__("torch").cuda.is_available(),
+                             reason="fake-pointer host tests run only without a GPU")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(D.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_missing_library_fails_loudly():
+    env = dict(os.environ, DECSTEP_LIB="/nonexistent/libdecstep.so")
+    r = subprocess.run([sys.executable, "-c", "import autoregressive_audio_token_amd"],
+                       cwd=ROOT, env=env, capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_strerror_names_every_status():
+    for code in range(8):
+        assert dec.dec_strerror(code).startswith("DEC_")
+    assert "unknown" in dec.dec_strerror(99)
+
+
+def _attn(**kw):
+    a = dict(q=A, k=A, v=A, len=A, out=A, NL=1, B=1, H=1, L=16, hd=64, dt=0, scale=0.125,
+             ws=None, wsb=0)
+    a.update(kw)
+    return D.raw_status("dec_attn_self", a["q"], a["k"], a["v"], a["len"], a["out"], a["NL"],
+                        a["B"], a["H"], a["L"], a["hd"], a["dt"], ctypes.c_float(a["scale"]),
+                        a["ws"], a["wsb"], None)
+
+
+@_no_gpu
+def test_attention_host_validation():
+    assert _attn(q=None) == D.DEC_E_NULL
+    assert _attn(len=None) == D.DEC_E_NULL
+    assert _attn(dt=2) == D.DEC_E_DTYPE
+    for bad in (dict(NL=0), dict(B=0), dict(H=-1), dict(L=0), dict(B=1 << 20, H=1 << 11)):
+        assert _attn(**bad) == D.DEC_E_SHAPE, bad
+    assert _attn(hd=128) == D.DEC_E_UNSUPPORTED
+    assert _attn(B=5000) == D.DEC_E_UNSUPPORTED
+    assert _attn(q=A + 8) == D.DEC_E_ALIGN
+    assert _attn(out=A + 2) == D.DEC_E_ALIGN
+    # a cache longer than one chunk needs the workspace
+    L = 4 * dec.dec_attn_chunk_keys()
+    need = dec.dec_attn_workspace_bytes(1, 1, 1, 64, L, 0)
+    assert need > 0
+    assert _attn(L=L, ws=None, wsb=0) == D.DEC_E_NULL
+    assert _attn(L=L, ws=A, wsb=need - 1) == D.DEC_E_WORKSPACE
+    assert _attn(L=L, ws=A + 4, wsb=need) == D.DEC_E_ALIGN
+
+
+@_no_gpu
+def test_step_validation_and_workspace_sizes():
+    st = D.raw_status("dec_attn_step", A, A, A, A, 4096, A, A, A, A, None, 64, A,
+                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, 16, None)
+    assert st == D.DEC_E_NULL
+    need = dec.dec_attn_workspace_bytes(24, 1, 16, 64, 4096, 1024)
+    st = D.raw_status("dec_attn_step", A, A, A, A, 4096, A, A, A, A, A, 1024, A,
+                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, need - 1, None)
+    assert st == D.DEC_E_WORKSPACE
+    ck = dec.dec_attn_chunk_keys()
+    # one chunk of capacity: no workspace at all
+    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, ck, ck) == 0
+    s = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 0)
+    c = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 0, 3 * ck)
+    assert dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 3 * ck) == s + c
+    assert s >= 24 * 10 * 68 * 4 and c >= 24 * 3 * 68 * 4
+    assert dec.dec_attn_workspace_bytes(2, 3, 4, 32, 10, 10) == 0
+
+
+def _samp(**kw):
+    a = dict(lg=A, B=1, ncb=9, V=1089, S=1096, T=A, k=50, u=A, step=None, fill=1089, tok=A,
+             idx=None, prob=None)
+    a.update(kw)
+    return D.raw_status("dec_sample_topk", a["lg"], a["B"], a["ncb"], a["V"], a["S"], a["T"],
+                        a["k"], a["u"], a["step"], a["fill"], a["tok"], a["idx"], a["prob"],
+                        None)
+
+
+@_no_gpu
+def test_sampler_host_validation():
+    assert _samp(lg=None) == D.DEC_E_NULL
+    assert _samp(u=None) == D.DEC_E_NULL
+    assert _samp(tok=None) == D.DEC_E_NULL
+    for bad in (dict(B=0), dict(ncb=0), dict(V=0), dict(S=1000), dict(k=0), dict(k=65)):
+        assert _samp(**bad) == D.DEC_E_SHAPE, bad
+    assert _samp(V=5000, S=5000) == D.DEC_E_UNSUPPORTED
+    assert _samp(lg=A + 2) == D.DEC_E_ALIGN
+    assert _samp(idx=A + 1) == D.DEC_E_ALIGN
+
+
+@_no_gpu
+def test_misc_validation():
+    assert D.raw_status("dec_step_advance", A, A, 0, None) == D.DEC_E_SHAPE
+    assert D.raw_status("dec_step_advance", None, None, 3, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_graph_begin", None) == D.DEC_E_NULL
+    assert D.raw_status("dec_graph_end", None, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_graph_launch", None, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_graph_destroy", None) == D.DEC_E_NULL
+    assert D.raw_status("dec_attn_workspace_init", None, 0, None) == D.DEC_OK
+    assert D.raw_status("dec_attn_workspace_init", None, 64, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_attn_workspace_init", A + 4, 64, None) == D.DEC_E_ALIGN
+
+
+def test_order_key_map_is_monotone_over_all_float32_bit_patterns():
+    # Every float32 bit pattern, in increasing order of value: -inf .. -0 then +0 .. +inf.
+    # Keys must increase strictly, except that -0 and +0 share a key; NaNs map outside
+    # [key(-inf), key(+inf)] by sign.
+    chunk = 1 << 25
+    prev = None
+    keys = np.empty(chunk, np.uint32)
+    # negative values: bit patterns 0xFF800000 down to 0x80000000
+    for hi in range(0xFF800000 + 1, 0x80000000, -chunk):
+        lo = max(hi - chunk, 0x80000000)
+        bits = np.arange(hi - 1, lo - 1, -1, dtype=np.int64).astype(np.uint32)
+        x = bits.view(np.float32)
+        k = keys[:x.size]
+        dec.dec_order_keys_host(x, k, x.size)
+        assert np.all(np.diff(k.astype(np.int64)) > 0)
+        if prev is not None:
+            assert int(k[0]) > prev
+        prev = int(k[-1])
+    kneg0 = prev
+    for lo in range(0, 0x7F800000 + 1, chunk):
+        hi = min(lo + chunk, 0x7F800000 + 1)
+        bits = np.arange(lo, hi, dtype=np.int64).astype(np.uint32)
+        x = bits.view(np.float32)
+        k = keys[:x.size]
+        dec.dec_order_keys_host(x, k, x.size)
+        assert np.all(np.diff(k.astype(np.int64)) > 0)
+        if lo == 0:
+            assert int(k[0]) == kneg0          # -0 and +0 tie
+        else:
+            assert int(k[0]) > prev
+        prev = int(k[-1])
+    kinf = prev
+    nan = np.array([0x7FC00000, 0x7F800001, 0xFFC00000, 0xFF800001], np.uint32).view(np.float32)
+    kn = np.zeros(4, np.uint32)
+    dec.dec_order_keys_host(nan, kn, 4)
+    x = np.array([-np.inf], np.float32)
+    kmin = np.zeros(1, np.uint32)
+    dec.dec_order_keys_host(x, kmin, 1)
+    assert kn[0] > kinf and kn[1] > kinf and kn[2] < kmin[0] and kn[3] < kmin[0]
