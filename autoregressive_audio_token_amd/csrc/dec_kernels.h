@@ -9,17 +9,19 @@ namespace dec {
 
 // ---- attention (split-K flash-decode over the valid prefix) ----------------------
 
-constexpr int kAttnWaves = 4;                       // waves per workgroup
-constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kAttnKeysPerWaveTile = 64;            // keys one wave loads per tile
-#ifndef DEC_ATTN_TILES
-#define DEC_ATTN_TILES 1
+#ifndef DEC_ATTN_WAVES
+#define DEC_ATTN_WAVES 16
 #endif
-constexpr int kAttnTiles = DEC_ATTN_TILES;          // tiles per wave per chunk
-constexpr int kAttnChunk = kAttnWaves * kAttnKeysPerWaveTile * kAttnTiles;
-constexpr int kAttnPartStride = 68;                 // floats per partial: m, l, pad, pad, acc[64]
+constexpr int kAttnWaves = DEC_ATTN_WAVES;          // waves per workgroup
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnKeysPerWave = 64;                // keys one wave loads per round
+constexpr int kAttnChunk = kAttnWaves * kAttnKeysPerWave;  // keys per chunk (one round)
+constexpr int kAttnPartStride = 68;                 // floats per chunk partial: m, l, pad, pad, acc[64]
 constexpr int kAttnHeadDim = 64;
 constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
+constexpr int kAttnSortMax = 1024;                  // groups ordered longest-first up to this count
+constexpr int kAttnSplitBelow = 512;                // split sequences across workgroups below this
+                                                    // many sequences per launch
 
 // One attention problem ("segment"): self-attention or cross-attention of a step.
 struct AttnSeg {
@@ -28,8 +30,7 @@ struct AttnSeg {
   const void* v;          // [NL, B, H, L_cap, 64]
   const int32_t* len;     // [B] valid slots
   float* out;             // [NL, B, H, 64]
-  float* part;            // [NL*B*H, nck_cap, kAttnPartStride] split-K partials (or null)
-  int32_t* ticket;        // [NL*B*H] arrival counters, zero between calls (or null)
+  float* part;            // [NL*B*H, nck_cap, kAttnPartStride] chunk partials (split mode)
   int L_cap;
   int nck_cap;            // ceil(L_cap / kAttnChunk)
 };
@@ -38,12 +39,14 @@ struct AttnParams {
   AttnSeg seg[2];
   int nseg;
   int NL, B, H;
+  int cpi;                // chunks per work item (>= nck_cap of every segment: no split)
   float qscale;           // scale * log2(e): scores are formed in base 2
 };
 
 // Upper bound on the work items of a launch (every sequence at full capacity).
 long long attn_items_cap(const AttnParams& p);
-// Enqueue the attention kernel; `blocks` <= 0 picks the occupancy-sized grid.
+// Enqueue the attention kernel (and, in split mode, the chunk combine kernel);
+// `blocks` <= 0 picks the occupancy-sized persistent grid.
 hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream);
 
 // ---- sampler ---------------------------------------------------------------------

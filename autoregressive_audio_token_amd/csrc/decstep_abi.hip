@@ -21,11 +21,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Workspace of one attention segment: arrival counters, then split-K partials.
-// Segments whose capacity fits one chunk need neither.
+// Workspace of one attention segment: the chunk partials used when a launch
+// spreads the chunks of a sequence over several workgroups.  Capacities that fit
+// one chunk need none.
 struct SegLayout {
-  size_t ticket_off = 0, part_off = 0, bytes = 0;
-  int nck_cap = 1;
+  size_t bytes = 0;
+  int nck_cap = 0;
 };
 
 SegLayout seg_layout(int NL, int B, int H, int L_cap) {
@@ -34,9 +35,7 @@ SegLayout seg_layout(int NL, int B, int H, int L_cap) {
   s.nck_cap = (L_cap + dec::kAttnChunk - 1) / dec::kAttnChunk;
   if (s.nck_cap <= 1) return s;
   const size_t nseq = (size_t)NL * B * H;
-  s.ticket_off = 0;
-  s.part_off = align_up(nseq * sizeof(int32_t), 256);
-  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
+  s.bytes = align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
   return s;
 }
 
@@ -48,12 +47,10 @@ bool sizes_ok(int NL, int B, int H, int L_cap) {
   return elems < (1LL << 46);
 }
 
-// Optional grid override for tuning and for grid-independence tests.
-int grid_override() {
-  const char* s = getenv("DECSTEP_ATTN_BLOCKS");
-  if (s == nullptr) return 0;
-  const int v = atoi(s);
-  return v > 0 ? v : 0;
+// Optional overrides for tuning and for the grid- and split-independence tests.
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s == nullptr ? dflt : atoi(s);
 }
 
 struct SegArgs {
@@ -99,6 +96,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   p.B = B;
   p.H = H;
   p.qscale = scale * 1.4426950408889634f;  // log2(e)
+  int nck_max = 1;
   size_t off = 0;
   for (int s = 0; s < nseg; ++s) {
     dec::AttnSeg& g = p.seg[s];
@@ -109,15 +107,17 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.out = segs[s].out;
     g.L_cap = segs[s].L_cap;
     g.nck_cap = lay[s].nck_cap;
-    if (lay[s].bytes > 0) {
-      char* base = static_cast<char*>(ws) + off;
-      g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
-      g.part = reinterpret_cast<float*>(base + lay[s].part_off);
-    }
+    if (lay[s].bytes > 0) g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
     off += lay[s].bytes;
+    if (lay[s].nck_cap > nck_max) nck_max = lay[s].nck_cap;
   }
+  // Few sequences: spread each sequence's chunks over workgroups (one chunk per
+  // item) so the chip fills; otherwise one workgroup owns a whole sequence.
+  const long long seqs = (long long)NL * B * H * nseg;
+  const int split = env_int("DECSTEP_ATTN_SPLIT", seqs < dec::kAttnSplitBelow ? 1 : 0);
+  p.cpi = split ? 1 : nck_max;
   if (nseg == 1) p.seg[1] = p.seg[0];
-  const hipError_t e = dec::attn_launch(p, dtype, grid_override(), stream);
+  const hipError_t e = dec::attn_launch(p, dtype, env_int("DECSTEP_ATTN_BLOCKS", 0), stream);
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
@@ -137,6 +137,7 @@ size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_se
 }
 
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {
+  // The workspace carries no state between calls; zeroing it is optional.
   if (ws_bytes == 0) return DEC_OK;
   if (workspace == nullptr) return DEC_E_NULL;
   if (!aligned(workspace, 16)) return DEC_E_ALIGN;

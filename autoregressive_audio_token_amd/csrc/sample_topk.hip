@@ -12,14 +12,16 @@
 // until the sequence has taken c steps.
 //
 // Per row (64 lanes):
-//   1. Stage the row through LDS so each lane owns a CONTIGUOUS run of VPL
-//      vocabulary entries (vocabulary order == lane order, then slot order).
+//   1. Each lane loads entries lane, lane + 64, lane + 128, ... (every load
+//      instruction is one coalesced 256-byte row segment; all are in flight at
+//      once).  Vocabulary order is (slot, lane) order.
 //   2. Map values to order-preserving uint32 keys and find the kk-th largest
 //      key by MSB-first bisection; each step counts keys >= candidate with
-//      wave ballots (exact, integer only).
-//   3. Keep keys above the threshold plus the lowest-index entries equal to it
-//      (a wave prefix count ranks ties in vocabulary order); compact the kept
-//      entries through LDS so lane t holds the t-th kept entry in ascending
+//      wave ballots (exact, integer only) and stops once exactly kk remain.
+//   3. Keep keys above the threshold plus the lowest-index entries equal to it.
+//      Ranks in vocabulary order come from ballots and mbcnt (the running
+//      count of earlier slots plus the set lanes below); kept entries are
+//      compacted through LDS so lane t holds the t-th kept entry in ascending
 //      vocabulary order (kk <= 64).
 //   4. e_t = exp((x_t - max) / T); wave inclusive scan; C_t = S_t / S_last;
 //      the token is the first kept entry with u < C_t.  T <= 0: greedy.
@@ -28,40 +30,43 @@
 
 namespace dec {
 
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0u));
+}
+
 template <int VPL>
 __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
-  constexpr int STR = VPL | 1;  // odd LDS stride: the contiguous-run reads do not conflict
-  extern __shared__ float s_buf[];
+  __shared__ float s_val[kSampWaves][kWave];
+  __shared__ int s_idx[kSampWaves][kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int rows = p.B * p.n_cb;
   const int row = blockIdx.x * kSampWaves + wave;
-  const bool active = row < rows;  // uniform per wave; inactive waves still reach barriers
+  const bool active = row < rows;  // uniform per wave; inactive waves still reach the barrier
+  const int kk = p.top_k < p.V_valid ? p.top_k : p.V_valid;
 
-  float* buf = s_buf + wave * (kWave * STR + 2 * kWave);
-  float* cval = buf + kWave * STR;
-  int* cidx = reinterpret_cast<int*>(cval + kWave);
+  // per-row scalars first, so their latency overlaps the logits' and the selection
+  const int b = active ? row / p.n_cb : 0;
+  const int c = active ? row - b * p.n_cb : 0;
+  const float T = active ? p.temperature[b] : 1.f;
+  const float u = active ? p.uniforms[row] : 0.f;
+  const int started = (active && p.step != nullptr) ? (p.step[b] >= c) : 1;
 
   if (active) {
     const float* x = p.logits + (size_t)row * p.V_stride;
-    for (int i = lane; i < p.V_valid; i += kWave) {
-      const int o = i / VPL;
-      buf[o * STR + (i - o * VPL)] = x[i];
-    }
-  }
-  __syncthreads();
-
-  const int kk = p.top_k < p.V_valid ? p.top_k : p.V_valid;
-  if (active) {
-    const int gbase = lane * VPL;
     float v[VPL];
     uint32_t key[VPL];
 #pragma unroll
+    for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
+      const int i = j * kWave + lane;
+      v[j] = x[i < p.V_valid ? i : p.V_valid - 1];
+    }
+#pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const bool ok = gbase + j < p.V_valid;
-      v[j] = ok ? buf[lane * STR + j] : 0.f;
-      key[j] = ok ? order_key(v[j]) : 0u;  // invalid slots: below every candidate
+      const int i = j * kWave + lane;
+      key[j] = i < p.V_valid ? order_key(v[j]) : 0u;  // absent entries: below every candidate
     }
     // threshold: the largest t with #(key >= t) >= kk, i.e. the kk-th largest key;
     // stop early once exactly kk keys are >= t
@@ -80,38 +85,29 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
 #pragma unroll
     for (int j = 0; j < VPL; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
     const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
-    int my_eq = 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) my_eq += (gbase + j < p.V_valid && key[j] == tau) ? 1 : 0;
-    int rank = wave_exclusive_sum_int(my_eq, lane);
-    bool kept[VPL];
-    int my_kept = 0;
+    int eq_before = 0, kept_before = 0;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const bool eq = gbase + j < p.V_valid && key[j] == tau;
-      kept[j] = key[j] > tau || (eq && rank < need);
-      rank += eq ? 1 : 0;
-      my_kept += kept[j] ? 1 : 0;
-    }
-    int off = wave_exclusive_sum_int(my_kept, lane);
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      if (kept[j]) {
-        cval[off] = v[j];
-        cidx[off] = gbase + j;
-        ++off;
+      const int i = j * kWave + lane;
+      const bool eq = i < p.V_valid && key[j] == tau;
+      const unsigned long long eqm = __ballot(eq);
+      const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
+      const unsigned long long km = __ballot(kept);
+      if (kept) {
+        const int pos = kept_before + lanes_below(km);
+        s_val[wave][pos] = v[j];
+        s_idx[wave][pos] = i;
       }
+      eq_before += __popcll(eqm);
+      kept_before += __popcll(km);
     }
   }
   __syncthreads();
 
   if (active) {
     const bool act = lane < kk;
-    const float xv = act ? cval[lane] : -INFINITY;
-    const int xi = act ? cidx[lane] : -1;
-    const int b = row / p.n_cb;
-    const int c = row - b * p.n_cb;
-    const float T = p.temperature[b];
+    const float xv = act ? s_val[wave][lane] : -INFINITY;
+    const int xi = act ? s_idx[wave][lane] : -1;
     const float m = wave_max(xv);
     int sel;
     float prob;
@@ -124,13 +120,12 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
       const float S = wave_inclusive_sum(e, lane);
       const float Z = __shfl(S, kk - 1);
       const float C = S / Z;
-      const float u = p.uniforms[row];
       const unsigned long long mk = __ballot(act && u < C);
       sel = mk ? __ffsll(mk) - 1 : kk - 1;
       prob = e / Z;
     }
     int token = __shfl(xi, sel);
-    if (p.step != nullptr && p.step[b] < c) token = p.fill;
+    if (!started) token = p.fill;
     if (lane == 0) p.tokens[row] = token;
     if (lane < p.top_k) {
       if (p.topk_idx != nullptr) p.topk_idx[(size_t)row * p.top_k + lane] = act ? xi : -1;
@@ -141,11 +136,9 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
 
 template <int VPL>
 static hipError_t sample_launch_vpl(const SampleParams& p, hipStream_t stream) {
-  constexpr int STR = VPL | 1;
   const int rows = p.B * p.n_cb;
   const int blocks = (rows + kSampWaves - 1) / kSampWaves;
-  const size_t lds = (size_t)kSampWaves * (kWave * STR + 2 * kWave) * sizeof(float);
-  hipLaunchKernelGGL(sample_topk_kernel<VPL>, dim3(blocks), dim3(kSampWaves * kWave), lds, stream, p);
+  hipLaunchKernelGGL(sample_topk_kernel<VPL>, dim3(blocks), dim3(kSampWaves * kWave), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -27,6 +27,11 @@ class DecError(RuntimeError):
 
 
 def _load():
+    # torch ships its own libamdhip64 under the same soname.  Importing torch first
+    # lets the dynamic loader bind this library to that same HIP runtime instance;
+    # loading ours first would put two HIP runtimes in one process, and the second
+    # one to initialise finds no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m autoregressive_audio_token_amd.build` "

@@ -55,23 +55,27 @@ enum dec_status {
   DEC_E_ALIGN = 7         /* a pointer is not aligned as required */
 };
 
-/* Keys per split-K chunk of the attention kernels: a sequence of n valid keys
- * is split into max(1, ceil(n / chunk)) chunks whose partial softmax states
- * are combined in chunk order.  The split depends on n only, never on the
- * grid, so results are bitwise reproducible run to run. */
+/* Keys per split-K chunk of the attention kernels.  A sequence of n valid
+ * keys is cut into ceil(n / chunk) chunks; each chunk's partial softmax state
+ * (max, sum, weighted values) is formed in a fixed order and the chunk states
+ * fold in chunk order.  The cut depends on n only, never on the grid or on how
+ * chunks are spread over workgroups, so results are bitwise reproducible. */
 int dec_attn_chunk_keys(void);
 
 /* Workspace bytes for attention over n_layers x B x H sequences with a self
  * cache of L_cap_self slots and a cross cache of L_cap_cross slots (pass 0 for
- * a cache that the call does not use).  One workspace sized for both serves
- * dec_attn_self, dec_attn_cross and dec_attn_step.  Returns 0 on bad sizes. */
+ * a cache that the call does not use).  The workspace holds chunk partials when
+ * a launch spreads a sequence over several workgroups (launches with few
+ * sequences do); capacities that fit one chunk need none.  One workspace sized
+ * for both caches serves dec_attn_self, dec_attn_cross and dec_attn_step.
+ * Returns 0 on bad sizes. */
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,
                                 int L_cap_self, int L_cap_cross);
 
-/* Zero a workspace (a fill kernel, not a memset, so it may be captured).
- * Required once after allocation; every attention call leaves the workspace's
- * counters at zero again when it completes.  Calls that share one workspace
- * must be ordered (same stream); concurrent use of one workspace races. */
+/* Zero a workspace with a fill kernel (capturable).  Optional: the attention
+ * calls keep no state in the workspace between calls.  Calls that share one
+ * workspace must be ordered (same stream); concurrent use of one workspace
+ * races. */
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream);
 
 /* Single-token self-attention over the valid prefix of a static KV cache
@@ -86,7 +90,7 @@ int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t strea
  *   hd must be 64; dtype is DEC_BF16 or DEC_F32; accumulation is float32.
  * Device-side values: len[b] <= 0 gives an all-zero output row; len[b] >
  * L_cap is read as L_cap.  n_layers > 1 means layer-stacked buffers served by
- * one launch. */
+ * one launch.  B is at most 4096 (2048 for dec_attn_step): DEC_E_UNSUPPORTED. */
 int dec_attn_self(const void* q, const void* k, const void* v, const int32_t* len,
                   float* out, int n_layers, int B, int H, int L_cap, int hd, int dtype,
                   float scale, void* workspace, size_t ws_bytes, dec_stream_t stream);

@@ -80,7 +80,8 @@ def test_parity_long_output_selected_steps():
             _check("cross", w, d, o_c, src, rows, d["cross_len_host"])
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 255, 256, 257, 511, 513, 1000, 4095, 4096])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 1000, 1023, 1024, 1025, 2047, 2048, 2049,
+                               3071, 4095, 4096])
 def test_ragged_lengths_and_chunk_edges(n):
     w = configs.MINI_V1
     lens = np.array([n], dtype=np.int32)
@@ -180,3 +181,36 @@ def test_fp32_tiny_with_invalid_slots_poisoned_by_inf():
     d = _inputs(w, invalid=float("inf"))
     src = RowSource(w, d["self_len_host"], d["cross_len_host"])
     _check("self", w, d, hp.attn("self", w, d), src, all_rows(w), d["self_len_host"])
+
+
+@pytest.mark.parametrize("n", [700, 1024, 1025, 3000, 4096])
+def test_split_and_whole_sequence_modes_agree_bitwise(n, monkeypatch):
+    # chunks spread over workgroups (folded by the combine kernel) versus one
+    # workgroup per sequence: identical arithmetic, identical bits
+    w = configs.MINI_V1
+    d = _inputs(w, self_lens=[n])
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "0")
+    whole = hp.host(hp.attn("self", w, d))
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
+    split = hp.host(hp.attn("self", w, d))
+    assert np.array_equal(whole, split)
+    src = RowSource(w, [n], d["cross_len_host"])
+    rows = sampled_rows(w, 24, seed=n)
+    _check("self", w, d, torch.from_numpy(split), src, rows, np.array([n]))
+
+
+def test_per_layer_calls_equal_the_stacked_call_bitwise():
+    # the model-shaped schedule: one call per layer on offset pointers (a launch of
+    # 16 sequences, which spreads chunks over workgroups) against one stacked launch
+    import autoregressive_audio_token_amd as dec
+    w = configs.LONG_OUTPUT
+    lens = np.array([2500], np.int32)
+    d = _inputs(w, self_lens=lens)
+    stacked = hp.host(hp.attn("self", w, d))
+    nb = dec.dec_attn_workspace_bytes(1, 1, w.heads, 64, w.self_cap, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=hp.DEV)
+    out = hp.out_buf(w)
+    for layer in range(w.n_layers):
+        dec.dec_attn_self(d["q_self"][layer], d["k_self"][layer], d["v_self"][layer], d["len"],
+                          out[layer], 1, 1, w.heads, w.self_cap, 64, dec.DEC_BF16, w.scale, ws, nb)
+    assert np.array_equal(hp.host(out), stacked)
