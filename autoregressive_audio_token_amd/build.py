@@ -27,6 +27,8 @@ def compile_flags(defines=()):
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              # no packed fp32 instructions in any generated code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # floating point exactly as written: fused multiply-adds only where fmaf says so
+             "-ffp-contract=off",
              "-Wall", "-Wno-unused-function",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     flags += [f"-D{d}" for d in defines]

@@ -7,31 +7,46 @@
 // bytes plus a few hundred bytes per sequence.
 //
 // Split-K flash-decode, arranged for CDNA4:
-//   * A sequence of n valid keys is cut into chunks of kAttnChunk keys.  One
-//     workgroup of kAttnWaves wavefronts reads a whole chunk in one round: each
-//     wave owns 64 keys and issues all of its K and V loads at once (a key row
-//     of 64 bf16 is 128 B = 8 lanes x 16 B, so one dwordx4 load instruction
-//     covers 8 consecutive keys, 1 KiB, fully coalesced).  There is no MFMA:
-//     the work is a GEMV.
-//   * Scores reduce across the 8 lanes of a key with DPP moves; softmax is in
-//     base 2 (q pre-scaled by scale * log2 e) and fp32 throughout.
-//   * The waves' partial states (max, sum, acc[64]) combine through LDS in
-//     wave order into one state per chunk; the chunk states of a sequence then
-//     fold in chunk order.  Normally one workgroup owns every chunk of its
-//     sequence, so nothing crosses workgroups (no atomics, no fences).  When a
-//     launch has few sequences, chunks are spread over workgroups, written to
-//     the workspace, and a second kernel performs the same fold; both paths
-//     execute identical arithmetic, so results are bitwise equal either way
-//     and independent of the grid.
-//   * The list of work items is derived on the device from len[] (device
+//   * A sequence of n valid keys is cut into chunks of kAttnChunk keys.  A
+//     workgroup of kAttnWaves wavefronts streams a chunk in tile rounds: in
+//     each round every wave reads a 64-key tile (a key row of 64 bf16 is 128 B
+//     = 8 lanes x 16 B, so one dwordx4 load instruction covers 8 consecutive
+//     keys, 1 KiB, fully coalesced), and the next tile's K and V loads are in
+//     flight while the current tile is computed (double buffering).  There is
+//     no MFMA: the work is a GEMV, bound by HBM.
+//   * Scores reduce across the 8 lanes of a key with DPP moves.  Each group of
+//     8 lanes keeps its own online-softmax state across the tiles (base 2, q
+//     pre-scaled by scale * log2 e, fp32), so a tile needs no cross-lane max.
+//     At the end of a chunk the groups merge with DPP/shuffle butterflies and
+//     the waves merge through LDS, in a fixed order, into one chunk state.
+//   * Chunk states of a sequence fold in chunk order.  Normally one workgroup
+//     owns every chunk of its sequence, so nothing crosses workgroups (no
+//     atomics, no fences).  When a launch has few sequences, chunks are spread
+//     over workgroups, written to the workspace, and a second kernel performs
+//     the same fold; both paths execute identical arithmetic, so results are
+//     bitwise equal either way and independent of the grid.
+//   * Short sequences are packed several to a workgroup (one or two waves
+//     each).  The work list is derived on the device from len[] (device
 //     resident, so a captured graph stays valid as lengths change), longest
-//     sequences first; a persistent grid of one workgroup per CU walks it.
+//     sequences first; a persistent, occupancy-sized grid walks it.
 #include "dec_common.h"
 #include "dec_kernels.h"
 
 namespace dec {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor word 3 for raw (untyped) buffer access on the gfx9 family,
+// and the cache-policy bit of a non-temporal access.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNonTemporal = 2;
+
+// A raw buffer over `rows` rows of `row_bytes` bytes starting at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows,
+                                                            int row_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, rows * row_bytes,
+                                           kBufWord3);
+}
 
 template <typename T>
 struct KvTraits;
@@ -57,15 +72,61 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&x)[4]) {
   x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
 }
 
-template <int EPL>
-__device__ __forceinline__ float dot_slice(const float (&q)[EPL], const u32x4& w) {
-  float x[EPL];
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A 32-bit word as two packed bf16.  Taken by value: bit-casting a vector-element
+// lvalue directly miscompiles to element 0 with this compiler.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// <q, k> over one 16-byte slice.  bf16: four packed bf16 pairs, each a
+// v_dot2c_f32_bf16 (products exact, fp32 accumulation); q stays packed bf16.
+// fp32: four fmas on q pre-converted to fp32.
+__device__ __forceinline__ float dot_slice(const u32x4& q, const u32x4& k) {
+  float s = 0.f;
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), s, false);
+  return s;
+}
+__device__ __forceinline__ float dot_slice(const float (&q)[4], const u32x4& w) {
+  float x[4];
   unpack(w, x);
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) s = fmaf(q[e], x[e], s);
+  for (int e = 0; e < 4; ++e) s = fmaf(q[e], x[e], s);
   return s;
 }
+
+// This lane's 16-byte slice of the query, and how a score is finished.
+template <typename T>
+struct QSlice;
+template <>
+struct QSlice<uint16_t> {  // packed bf16; the scale is applied to the finished score
+  u32x4 q;
+  float scale;
+  __device__ __forceinline__ void load(const uint16_t* qp, float qscale) {
+    q = *reinterpret_cast<const u32x4*>(qp);
+    scale = qscale;
+  }
+  __device__ __forceinline__ float dot(const u32x4& k) const { return dot_slice(q, k); }
+  __device__ __forceinline__ float finish(float s) const { return s * scale; }
+};
+template <>
+struct QSlice<float> {  // fp32, pre-scaled
+  float q[4];
+  __device__ __forceinline__ void load(const float* qp, float qscale) {
+    unpack(*reinterpret_cast<const u32x4*>(qp), q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] *= qscale;
+  }
+  __device__ __forceinline__ float dot(const u32x4& k) const { return dot_slice(q, k); }
+  __device__ __forceinline__ float finish(float s) const { return s; }
+};
+
+// 2^x by the hardware exponential (results below the fp32 normal range flush to 0,
+// a relative weight under 1e-38 that no output can show).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int EPL>
 __device__ __forceinline__ void accum_slice(float (&acc)[EPL], float p, const u32x4& w) {
@@ -88,7 +149,7 @@ __device__ __forceinline__ int items_per_lh(int n, int cpi) {
 // Shorter sequences are packed kAttnWaves / S to a work item.
 __device__ __forceinline__ int waves_per_seq(int n) {
   int s = 1;
-  while (s < kAttnWaves && s * kAttnKeysPerWave < n) s <<= 1;
+  while (s < kAttnWaves && s * kAttnKeysPerTile < n) s <<= 1;
   return s;
 }
 
@@ -113,20 +174,73 @@ __device__ __forceinline__ void fold_chunk(bool first, float mc, float lc, float
     return;
   }
   const float mn = fmaxf(m, mc);
-  const float fa = exp2f(m - mn);
-  const float fc = exp2f(mc - mn);
+  const float fa = exp2_hw(m - mn);
+  const float fc = exp2_hw(mc - mn);
   l = fmaf(lc, fc, l * fa);
   a = fmaf(ac, fc, a * fa);
   m = mn;
 }
 
+// One wave's view of a tile: NLD loads per operand, each covering KPL keys.
+template <typename T>
+struct Tile {
+  static constexpr int EPL = KvTraits<T>::kElemsPerLoad;  // elements per lane per load
+  static constexpr int LPK = kAttnHeadDim / EPL;          // lanes per key row: 8 (bf16), 16 (f32)
+  static constexpr int KPL = kWave / LPK;                 // keys per wave-wide load
+  static constexpr int NLD = kAttnKeysPerTile / KPL;      // loads per operand per tile
+  u32x4 k[NLD], v[NLD];
+
+  // Buffer loads through a descriptor that spans exactly the sequence's valid
+  // prefix (n rows): rows at or past n fall outside the descriptor's range and
+  // return zero without touching memory (their scores are masked to -inf in
+  // consume).  lane_off is this lane's byte offset inside a wave-wide load.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                       int base, int lane_off) {
+    constexpr int kRowBytes = kAttnHeadDim * (int)sizeof(T);
+    const int tile_off = base * kRowBytes + lane_off;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int off = tile_off + i * KPL * kRowBytes;
+      // K and V are read once: non-temporal
+      k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kBufNonTemporal);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kBufNonTemporal);
+    }
+  }
+
+  // Online-softmax update of this lane group's state (m, l, acc) with the tile.
+  __device__ __forceinline__ void consume(const QSlice<T>& qs, int base, int n, int kg,
+                                          float& m, float& l, float (&acc)[EPL]) const {
+    float s[NLD];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      s[i] = qs.finish(group_sum<LPK>(qs.dot(k[i])));
+      if (base + i * KPL + kg >= n) s[i] = -INFINITY;
+      tmax = fmaxf(tmax, s[i]);
+    }
+    if (tmax == -INFINITY) return;  // no valid key of this group in the tile
+    const float mn = fmaxf(m, tmax);
+    const float corr = exp2_hw(m - mn);  // 0 while m is still -inf
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const float pj = exp2_hw(s[i] - mn);
+      l += pj;
+      accum_slice(acc, pj, v[i]);
+    }
+    m = mn;
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p) {
   constexpr int HD = kAttnHeadDim;
-  constexpr int EPL = KvTraits<T>::kElemsPerLoad;  // elements per lane per load
-  constexpr int LPK = HD / EPL;                     // lanes per key row: 8 (bf16), 16 (f32)
-  constexpr int KPL = kWave / LPK;                  // keys per wave-wide load
-  constexpr int NLD = kAttnKeysPerWave / KPL;       // loads per operand per round
+  using TileT = Tile<T>;
+  constexpr int EPL = TileT::EPL;
+  constexpr int LPK = TileT::LPK;
+  constexpr int TPC = kAttnTilesPerChunk;
 
   extern __shared__ int s_dyn[];  // [G] lengths, [G] order, [G+1] item prefix
   __shared__ float s_acc[kAttnWaves][HD];
@@ -146,34 +260,65 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   int* s_pref = s_dyn + 2 * G;
 
   // ---- item list: groups (segment, b) longest first; group_items(n) each -------------
-  for (int g = tid; g < G; g += kAttnThreads) {
-    const bool cross = g >= B;
-    const int32_t* len = cross ? p.seg[1].len : p.seg[0].len;
-    const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
-    int n = len[cross ? g - B : g];
-    s_n[g] = n < 0 ? 0 : (n > cap ? cap : n);
-  }
-  __syncthreads();
-  for (int g = tid; g < G; g += kAttnThreads) {
-    int rank = g;
-    if (G <= kAttnSortMax) {  // stable rank by descending length
-      const int ng = s_n[g];
-      rank = 0;
-      for (int j = 0; j < G; ++j) {
-        const int nj = s_n[j];
-        rank += (nj > ng || (nj == ng && j < g)) ? 1 : 0;
+  if (G <= kWave) {
+    // One group per lane of wave 0; the other waves go straight to the barrier.
+    if (wave == 0) {
+      int n = 0, items = 0;
+      if (lane < G) {
+        const bool cross = lane >= B;
+        const int32_t* len = cross ? p.seg[1].len : p.seg[0].len;
+        const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
+        n = len[cross ? lane - B : lane];
+        n = n < 0 ? 0 : (n > cap ? cap : n);
+        items = group_items(n, NLH, cpi);
       }
+      int rank = 0;  // stable rank by descending length
+      for (int j = 0; j < G; ++j) {
+        const int nj = __shfl(n, j);
+        rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
+      }
+      if (lane < G) {
+        s_n[lane] = n;
+        s_order[rank] = lane;
+        s_pref[rank + 1] = items;  // scanned in place below
+      }
+      if (lane == 0) s_pref[0] = 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int v = lane < G ? s_pref[lane + 1] : 0;
+      const int incl = wave_inclusive_sum_int(v, lane);
+      if (lane < G) s_pref[lane + 1] = incl;
     }
-    s_order[rank] = g;
-  }
-  __syncthreads();
-  {
+    __syncthreads();
+  } else {
+    for (int g = tid; g < G; g += kAttnThreads) {
+      const bool cross = g >= B;
+      const int32_t* len = cross ? p.seg[1].len : p.seg[0].len;
+      const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
+      int n = len[cross ? g - B : g];
+      s_n[g] = n < 0 ? 0 : (n > cap ? cap : n);
+    }
+    __syncthreads();
+    for (int g = tid; g < G; g += kAttnThreads) {
+      int rank = g;
+      if (G <= kAttnSortMax) {  // stable rank by descending length
+        const int ng = s_n[g];
+        rank = 0;
+        for (int j = 0; j < G; ++j) {
+          const int nj = s_n[j];
+          rank += (nj > ng || (nj == ng && j < g)) ? 1 : 0;
+        }
+      }
+      s_order[rank] = g;
+    }
+    __syncthreads();
     const int per = (G + kAttnThreads - 1) / kAttnThreads;
     const int lo = min(G, tid * per);
     const int hi = min(G, lo + per);
     int local = 0;
     for (int i = lo; i < hi; ++i) local += group_items(s_n[s_order[i]], NLH, cpi);
-    int ex = wave_exclusive_sum_int(local, lane);
+    int ex = wave_inclusive_sum_int(local, lane) - local;
     if (lane == kWave - 1) s_wsum[wave] = ex + local;
     __syncthreads();
     int total = 0;
@@ -190,7 +335,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   }
   const int total = s_pref[G];
 
-  const int kg = lane / LPK;  // key slot within a wave-wide load
+  const int kg = lane / LPK;  // key slot within a wave-wide load (lane group)
   const int dl = lane % LPK;  // which 16-byte slice of the row this lane reads
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -211,14 +356,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const bool packed = spw < kAttnWaves;        // several sequences share this item
     const int P = kAttnWaves / spw;              // sequences in this item (packed)
 
-    // this wave's sequence and which 64-key slice of each round it reads
+    // this wave's sequence and its first key within each chunk
     int wave_lh, wave_part, c0, c1;
     bool whole;
-    if (packed) {
+    if (packed) {  // one tile per wave, one chunk
       wave_lh = r * P + wave / spw;
       wave_part = wave % spw;
       c0 = 0;
-      c1 = nck;  // at most one chunk
+      c1 = nck;
       whole = true;
     } else {
       const int ipl = items_per_lh(n, cpi);
@@ -253,52 +398,41 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     float fm = 0.f, fl = 0.f, fa = 0.f;  // running fold (combining threads)
 
     for (int c = c0; c < c1; ++c) {
-      const int base = c * kAttnChunk + wave_part * kAttnKeysPerWave;
-      float m_w = -INFINITY, l_w = 0.f;
+      // tile t of this wave starts at key tile_base(t); packed items read one tile
+      const int cb = c * kAttnChunk + wave_part * kAttnKeysPerTile;
+      float m_g = -INFINITY, l_g = 0.f;  // this lane group's online state
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-      if (wave_ok && base < n) {  // uniform across the wave
-        u32x4 kr[NLD], vr[NLD];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          const int j = base + i * KPL + kg;
-          if (j < n) {  // K and V are read once: non-temporal loads
-            kr[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(kp + (size_t)j * HD + dl * EPL));
-            vr[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(vp + (size_t)j * HD + dl * EPL));
-          } else {
-            kr[i] = u32x4{0u, 0u, 0u, 0u};
-            vr[i] = u32x4{0u, 0u, 0u, 0u};
-          }
+      if (wave_ok && cb < n) {  // uniform across the wave
+        constexpr int kStep = kAttnWaves * kAttnKeysPerTile;  // keys between a wave's tiles
+        constexpr int kRowBytes = HD * (int)sizeof(T);
+        const int nt = packed ? 1 : min(TPC, (n - cb + kStep - 1) / kStep);
+        const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kp, n, kRowBytes);
+        const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vp, n, kRowBytes);
+        const int lane_off = kg * kRowBytes + dl * 16;
+        TileT ta, tb;
+        ta.load(rk, rv, cb, lane_off);
+        QSlice<T> qs;
+        qs.load(qp + dl * EPL, p.qscale);
+        // ping-pong: the next tile is in flight while one is consumed (past the
+        // last tile the prefetch lies wholly outside the descriptor: no traffic)
+#pragma nounroll
+        for (int t = 0; t < nt; t += 2) {
+          const int base = cb + t * kStep;
+          tb.load(rk, rv, base + kStep, lane_off);
+          ta.consume(qs, base, n, kg, m_g, l_g, acc);
+          if (t + 1 >= nt) break;
+          ta.load(rk, rv, base + 2 * kStep, lane_off);
+          tb.consume(qs, base + kStep, n, kg, m_g, l_g, acc);
         }
-        float qf[EPL];
-        {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(qp + dl * EPL);
-          unpack(w, qf);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) qf[e] *= p.qscale;
-        }
-        float s[NLD];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          s[i] = group_sum<LPK>(dot_slice(qf, kr[i]));
-          if (base + i * KPL + kg >= n) s[i] = -INFINITY;
-          m_w = fmaxf(m_w, s[i]);
-        }
-        m_w = xor_max_from<LPK>(m_w);  // finite: key `base` is valid
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          const float pj = exp2f(s[i] - m_w);
-          l_w += pj;
-          accum_slice(acc, pj, vr[i]);
-        }
-        // sum the key groups of the wave (they share the wave max)
-        l_w = xor_sum_from<LPK>(l_w);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = xor_sum_from<LPK>(acc[e]);
       }
+      // merge the lane groups of the wave, in butterfly order
+      const float m_w = xor_max_from<LPK>(m_g);
+      const float f = (m_g == -INFINITY) ? 0.f : exp2_hw(m_g - m_w);
+      const float l_w = xor_sum_from<LPK>(l_g * f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = xor_sum_from<LPK>(acc[e] * f);
       if (kg == 0) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) s_acc[wave][dl * EPL + e] = acc[e];
@@ -315,9 +449,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
         for (int w = w0 + 1; w < w1; ++w) mc = fmaxf(mc, s_m[w]);
         float lc = 0.f, ac = 0.f;
         for (int w = w0; w < w1; ++w) {
-          const float f = (s_m[w] == -INFINITY) ? 0.f : exp2f(s_m[w] - mc);
-          lc = fmaf(f, s_l[w], lc);
-          ac = fmaf(f, s_acc[w][d], ac);
+          const float fw = (s_m[w] == -INFINITY) ? 0.f : exp2_hw(s_m[w] - mc);
+          lc = fmaf(fw, s_l[w], lc);
+          ac = fmaf(fw, s_acc[w][d], ac);
         }
         if (whole) {
           fold_chunk(c == c0, mc, lc, ac, fm, fl, fa);

@@ -60,24 +60,49 @@ __device__ __forceinline__ float wave_max(float v) {
   return xor_max_from<16>(v);
 }
 
-// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele, fixed order).
-__device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    float y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
+// Inclusive prefix sums over the 64 lanes in lane order, with DPP row shifts and
+// row broadcasts (the lanes a step does not update take a zero addend).  The
+// addition order is fixed, so results are reproducible.
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr3 = 0x113;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int dpp_i32_masked(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+__device__ __forceinline__ int wave_inclusive_sum_int(int v, int /*lane*/) {
+  const int x = v;
+  v += dpp_i32_masked<kDppRowShr1, 0xF, 0xF>(x);
+  v += dpp_i32_masked<kDppRowShr2, 0xF, 0xF>(x);
+  v += dpp_i32_masked<kDppRowShr3, 0xF, 0xF>(x);
+  v += dpp_i32_masked<kDppRowShr4, 0xF, 0xE>(v);
+  v += dpp_i32_masked<kDppRowShr8, 0xF, 0xC>(v);
+  v += dpp_i32_masked<kDppRowBcast15, 0xA, 0xF>(v);
+  v += dpp_i32_masked<kDppRowBcast31, 0xC, 0xF>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_inclusive_sum(float v, int /*lane*/) {
+  const int x = __builtin_bit_cast(int, v);
+  auto add = [](float a, int b) { return a + __builtin_bit_cast(float, b); };
+  v = add(v, dpp_i32_masked<kDppRowShr1, 0xF, 0xF>(x));
+  v = add(v, dpp_i32_masked<kDppRowShr2, 0xF, 0xF>(x));
+  v = add(v, dpp_i32_masked<kDppRowShr3, 0xF, 0xF>(x));
+  v = add(v, dpp_i32_masked<kDppRowShr4, 0xF, 0xE>(__builtin_bit_cast(int, v)));
+  v = add(v, dpp_i32_masked<kDppRowShr8, 0xF, 0xC>(__builtin_bit_cast(int, v)));
+  v = add(v, dpp_i32_masked<kDppRowBcast15, 0xA, 0xF>(__builtin_bit_cast(int, v)));
+  v = add(v, dpp_i32_masked<kDppRowBcast31, 0xC, 0xF>(__builtin_bit_cast(int, v)));
   return v;
 }
 
 __device__ __forceinline__ int wave_exclusive_sum_int(int v, int lane) {
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x - v;
+  return wave_inclusive_sum_int(v, lane) - v;
 }
 
 // ---- element decoding ------------------------------------------------------------

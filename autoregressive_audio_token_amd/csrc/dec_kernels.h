@@ -10,12 +10,18 @@ namespace dec {
 // ---- attention (split-K flash-decode over the valid prefix) ----------------------
 
 #ifndef DEC_ATTN_WAVES
-#define DEC_ATTN_WAVES 16
+#define DEC_ATTN_WAVES 4
 #endif
 constexpr int kAttnWaves = DEC_ATTN_WAVES;          // waves per workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kAttnKeysPerWave = 64;                // keys one wave loads per round
-constexpr int kAttnChunk = kAttnWaves * kAttnKeysPerWave;  // keys per chunk (one round)
+#ifndef DEC_ATTN_TILE_KEYS
+#define DEC_ATTN_TILE_KEYS 64
+#endif
+constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile
+constexpr int kAttnChunk = 1024;                    // keys per chunk
+constexpr int kAttnTilesPerChunk = kAttnChunk / (kAttnWaves * kAttnKeysPerTile);
+static_assert(kAttnTilesPerChunk * kAttnWaves * kAttnKeysPerTile == kAttnChunk,
+              "a chunk is a whole number of workgroup tile rounds");
 constexpr int kAttnPartStride = 68;                 // floats per chunk partial: m, l, pad, pad, acc[64]
 constexpr int kAttnHeadDim = 64;
 constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
