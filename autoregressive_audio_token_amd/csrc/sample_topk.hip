@@ -14,15 +14,19 @@
 // Per row (64 lanes):
 //   1. Each lane loads entries lane, lane + 64, lane + 128, ... (every load
 //      instruction is one coalesced 256-byte row segment; all are in flight at
-//      once).  Vocabulary order is (slot, lane) order.
-//   2. Map values to order-preserving uint32 keys and find the kk-th largest
-//      key by MSB-first bisection; each step counts keys >= candidate with
-//      wave ballots (exact, integer only) and stops once exactly kk remain.
-//   3. Keep keys above the threshold plus the lowest-index entries equal to it.
-//      Ranks in vocabulary order come from ballots and mbcnt (the running
-//      count of earlier slots plus the set lanes below); kept entries are
-//      compacted through LDS so lane t holds the t-th kept entry in ascending
-//      vocabulary order (kk <= 64).
+//      once).  Vocabulary order is (slot, lane) order.  Values map to
+//      order-preserving uint32 keys.
+//   2. Prune: the kk-th largest of the 64 per-lane maxima is a lower bound L0
+//      on the kk-th largest key (at least kk keys reach it), so keys below L0
+//      are never kept.  The survivors (typically under a tenth of the row) are
+//      compacted through LDS, still in vocabulary order, to at most kSurvSlots
+//      per lane; if more survive, the full row is searched instead.
+//   3. Exact threshold: MSB-first bisection for the kk-th largest key; each step
+//      counts keys >= candidate with wave ballots and stops once exactly kk
+//      remain.  Keys above it are kept, plus the lowest-index keys equal to it;
+//      ranks in vocabulary order come from ballots and mbcnt, and the kept
+//      entries are compacted through LDS so lane t holds the t-th kept entry in
+//      ascending vocabulary order (kk <= 64).
 //   4. e_t = exp((x_t - max) / T); wave inclusive scan; C_t = S_t / S_last;
 //      the token is the first kept entry with u < C_t.  T <= 0: greedy.
 #include "dec_common.h"
@@ -30,15 +34,61 @@
 
 namespace dec {
 
+constexpr int kSurvSlots = 3;  // survivor slots per lane after pruning
+
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0u));
+}
+
+// Exact top-kk over NS slots per lane, slot-major order = vocabulary order.
+// Absent slots carry key 0 and ok = false.  Writes the kept (value, index)
+// pairs, in order, to cval/cidx[0..kk).
+template <int NS>
+__device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const float (&val)[NS],
+                                            const int (&idx)[NS], int kk, float* cval,
+                                            int* cidx) {
+  // the largest t with #(key >= t) >= kk, i.e. the kk-th largest key; stop early
+  // once exactly kk keys are >= t
+  uint32_t tau = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= kk) {
+      tau = cand;
+      if (cnt == kk) break;
+    }
+  }
+  int cnt_gt = 0;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
+  const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
+  int eq_before = 0, kept_before = 0;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const bool eq = idx[j] >= 0 && key[j] == tau;
+    const unsigned long long eqm = __ballot(eq);
+    const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
+    const unsigned long long km = __ballot(kept);
+    if (kept) {
+      const int pos = kept_before + lanes_below(km);
+      cval[pos] = val[j];
+      cidx[pos] = idx[j];
+    }
+    eq_before += __popcll(eqm);
+    kept_before += __popcll(km);
+  }
 }
 
 template <int VPL>
 __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
   __shared__ float s_val[kSampWaves][kWave];
   __shared__ int s_idx[kSampWaves][kWave];
+  __shared__ uint32_t s_skey[kSampWaves][kSurvSlots * kWave];
+  __shared__ float s_sval[kSampWaves][kSurvSlots * kWave];
+  __shared__ int s_sidx[kSampWaves][kSurvSlots * kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -58,48 +108,63 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     const float* x = p.logits + (size_t)row * p.V_stride;
     float v[VPL];
     uint32_t key[VPL];
+    int idx[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
       const int i = j * kWave + lane;
       v[j] = x[i < p.V_valid ? i : p.V_valid - 1];
     }
+    uint32_t lmax = 0u;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int i = j * kWave + lane;
-      key[j] = i < p.V_valid ? order_key(v[j]) : 0u;  // absent entries: below every candidate
+      const bool ok = i < p.V_valid;
+      key[j] = ok ? order_key(v[j]) : 0u;  // absent entries: below every candidate
+      idx[j] = ok ? i : -1;
+      lmax = key[j] > lmax ? key[j] : lmax;
     }
-    // threshold: the largest t with #(key >= t) >= kk, i.e. the kk-th largest key;
-    // stop early once exactly kk keys are >= t
-    uint32_t tau = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-      if (cnt >= kk) {
-        tau = cand;
-        if (cnt == kk) break;
-      }
+    // L0: the kk-th largest lane maximum, to 16 leading bits (a lower bound either way)
+    uint32_t l0 = 0u;
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t cand = l0 | (1u << bit);
+      if (__popcll(__ballot(lmax >= cand)) >= kk) l0 = cand;
     }
-    int cnt_gt = 0;
+    int nsurv = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
-    const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
-    int eq_before = 0, kept_before = 0;
+    for (int j = 0; j < VPL; ++j) nsurv += __popcll(__ballot(idx[j] >= 0 && key[j] >= l0));
+
+    if (nsurv <= kSurvSlots * kWave) {
+      // compact the survivors in vocabulary order, then select among them
+      int base = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int i = j * kWave + lane;
-      const bool eq = i < p.V_valid && key[j] == tau;
-      const unsigned long long eqm = __ballot(eq);
-      const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
-      const unsigned long long km = __ballot(kept);
-      if (kept) {
-        const int pos = kept_before + lanes_below(km);
-        s_val[wave][pos] = v[j];
-        s_idx[wave][pos] = i;
+      for (int j = 0; j < VPL; ++j) {
+        const bool sv = idx[j] >= 0 && key[j] >= l0;
+        const unsigned long long m = __ballot(sv);
+        if (sv) {
+          const int pos = base + lanes_below(m);
+          s_skey[wave][pos] = key[j];
+          s_sval[wave][pos] = v[j];
+          s_sidx[wave][pos] = idx[j];
+        }
+        base += __popcll(m);
       }
-      eq_before += __popcll(eqm);
-      kept_before += __popcll(km);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint32_t sk[kSurvSlots];
+      float sv[kSurvSlots];
+      int si[kSurvSlots];
+#pragma unroll
+      for (int j = 0; j < kSurvSlots; ++j) {
+        const int q = j * kWave + lane;
+        const bool ok = q < nsurv;
+        sk[j] = ok ? s_skey[wave][q] : 0u;
+        sv[j] = ok ? s_sval[wave][q] : 0.f;
+        si[j] = ok ? s_sidx[wave][q] : -1;
+      }
+      select_kept(sk, sv, si, kk, s_val[wave], s_idx[wave]);
+    } else {
+      select_kept(key, v, idx, kk, s_val[wave], s_idx[wave]);
     }
   }
   __syncthreads();
