@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       }
       int rank = 0;  // stable rank by descending length
       for (int j = 0; j < G; ++j) {
-        const int nj = __shfl(n, j);
+        const int nj = __builtin_amdgcn_readlane(n, j);
         rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
       }
       if (lane < G) {

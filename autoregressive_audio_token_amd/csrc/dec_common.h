@@ -36,28 +36,36 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Butterfly across lanes that differ in bit positions [log2(FROM), 6): combines the
 // values held by lanes lane ^ FROM, lane ^ 2*FROM, ... (all lanes end with the result).
+// (The gfx950 permlane16/32 swaps would do the 16- and 32-lane steps in one VALU
+// op, but this compiler folds their two results as equal when both inputs are the
+// same value, so the steps use shuffles.)
 template <int FROM>
 __device__ __forceinline__ float xor_max_from(float v) {
   if constexpr (FROM <= 8) v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
   if constexpr (FROM <= 16) v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
 template <int FROM>
 __device__ __forceinline__ float xor_sum_from(float v) {
   if constexpr (FROM <= 8) v += dpp_f32<kDppRowRor8>(v);
   if constexpr (FROM <= 16) v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  return v + __shfl_xor(v, 32);
 }
 
+// Maximum over the wave, returned to every lane: DPP within each 16-lane row,
+// then the four row results through readlane.
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
   v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
   v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
   v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-  return xor_max_from<16>(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Inclusive prefix sums over the 64 lanes in lane order, with DPP row shifts and

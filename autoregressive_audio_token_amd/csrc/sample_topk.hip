@@ -123,31 +123,27 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
       idx[j] = ok ? i : -1;
       lmax = key[j] > lmax ? key[j] : lmax;
     }
-    // L0: the kk-th largest lane maximum, to 16 leading bits (a lower bound either way)
+    // L0: the kk-th largest lane maximum, to its 10 leading bits (a lower bound either way)
     uint32_t l0 = 0u;
-    for (int bit = 31; bit >= 16; --bit) {
+    for (int bit = 31; bit >= 22; --bit) {
       const uint32_t cand = l0 | (1u << bit);
       if (__popcll(__ballot(lmax >= cand)) >= kk) l0 = cand;
     }
+    // compact the survivors in vocabulary order (as long as they fit)
     int nsurv = 0;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) nsurv += __popcll(__ballot(idx[j] >= 0 && key[j] >= l0));
-
-    if (nsurv <= kSurvSlots * kWave) {
-      // compact the survivors in vocabulary order, then select among them
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const bool sv = idx[j] >= 0 && key[j] >= l0;
-        const unsigned long long m = __ballot(sv);
-        if (sv) {
-          const int pos = base + lanes_below(m);
-          s_skey[wave][pos] = key[j];
-          s_sval[wave][pos] = v[j];
-          s_sidx[wave][pos] = idx[j];
-        }
-        base += __popcll(m);
+    for (int j = 0; j < VPL; ++j) {
+      const bool sv = idx[j] >= 0 && key[j] >= l0;
+      const unsigned long long m = __ballot(sv);
+      const int pos = nsurv + lanes_below(m);
+      if (sv && pos < kSurvSlots * kWave) {
+        s_skey[wave][pos] = key[j];
+        s_sval[wave][pos] = v[j];
+        s_sidx[wave][pos] = idx[j];
       }
+      nsurv += __popcll(m);
+    }
+    if (nsurv <= kSurvSlots * kWave) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -163,7 +159,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
         si[j] = ok ? s_sidx[wave][q] : -1;
       }
       select_kept(sk, sv, si, kk, s_val[wave], s_idx[wave]);
-    } else {
+    } else {  // too many survivors (heavy ties or a flat row): search the whole row
       select_kept(key, v, idx, kk, s_val[wave], s_idx[wave]);
     }
   }
@@ -183,13 +179,13 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     } else {
       const float e = act ? expf((xv - m) / T) : 0.f;
       const float S = wave_inclusive_sum(e, lane);
-      const float Z = __shfl(S, kk - 1);
+      const float Z = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kk - 1));
       const float C = S / Z;
       const unsigned long long mk = __ballot(act && u < C);
       sel = mk ? __ffsll(mk) - 1 : kk - 1;
       prob = e / Z;
     }
-    int token = __shfl(xi, sel);
+    int token = __builtin_amdgcn_readlane(xi, sel);
     if (!started) token = p.fill;
     if (lane == 0) p.tokens[row] = token;
     if (lane < p.top_k) {
