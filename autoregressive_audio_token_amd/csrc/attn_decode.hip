@@ -19,12 +19,16 @@
 //     pre-scaled by scale * log2 e, fp32), so a tile needs no cross-lane max.
 //     At the end of a chunk the groups merge with DPP/shuffle butterflies and
 //     the waves merge through LDS, in a fixed order, into one chunk state.
-//   * Chunk states of a sequence fold in chunk order.  Normally one workgroup
-//     owns every chunk of its sequence, so nothing crosses workgroups (no
-//     atomics, no fences).  When a launch has few sequences, chunks are spread
-//     over workgroups, written to the workspace, and a second kernel performs
-//     the same fold; both paths execute identical arithmetic, so results are
-//     bitwise equal either way and independent of the grid.
+//   * Chunk states of a sequence fold in chunk order.  When a launch has many
+//     sequences, one workgroup owns every chunk of its sequence and folds in
+//     registers: nothing crosses workgroups.  When it has few, every chunk is
+//     its own work item (so the CUs get equal bytes): the chunk's workgroup
+//     writes its state with agent-coherent (write-through) stores, waits for
+//     them, and takes a ticket with an agent-scope atomic; the last to arrive
+//     reads every chunk state with agent-coherent loads, folds them in chunk
+//     order and resets the ticket.  No L2 write-back or invalidate is needed,
+//     and both modes fold the same fp32 chunk states in the same order, so
+//     results are bitwise equal either way and independent of the grid.
 //   * Short sequences are packed several to a workgroup (one or two waves
 //     each).  The work list is derived on the device from len[] (device
 //     resident, so a captured graph stays valid as lengths change), longest
@@ -247,6 +251,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   __shared__ float s_m[kAttnWaves];
   __shared__ float s_l[kAttnWaves];
   __shared__ int s_wsum[kAttnWaves];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -455,41 +460,48 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
         }
         if (whole) {
           fold_chunk(c == c0, mc, lc, ac, fm, fl, fa);
-        } else {
+        } else {  // publish the chunk state, write-through
           float* pp = S.part + (slot_sidx * S.nck_cap + c) * kAttnPartStride;
-          pp[4 + d] = ac;
+          __hip_atomic_store(pp + 4 + d, ac, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (d == 0) {
-            pp[0] = mc;
-            pp[1] = lc;
+            __hip_atomic_store(pp, mc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pp + 1, lc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
       __syncthreads();  // LDS is rewritten by the next chunk
     }
-    if (whole && slot_ok) S.out[slot_sidx * HD + d] = fa / fl;
+    if (whole) {
+      if (slot_ok) S.out[slot_sidx * HD + d] = fa / fl;
+      continue;
+    }
+    // split mode (one chunk per item): every thread's stores have completed before
+    // the ticket is taken; the last chunk to arrive folds them all in chunk order
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int prev =
+          __hip_atomic_fetch_add(S.ticket + slot_sidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == nck - 1;
+    }
+    __syncthreads();
+    if (s_last) {
+      if (slot_ok) {
+        const float* pp = S.part + slot_sidx * S.nck_cap * kAttnPartStride;
+        for (int cc = 0; cc < nck; ++cc) {
+          const float* q = pp + cc * kAttnPartStride;
+          const float mc = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float lc = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float ac = __hip_atomic_load(q + 4 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          fold_chunk(cc == 0, mc, lc, ac, fm, fl, fa);
+        }
+        S.out[slot_sidx * HD + d] = fa / fl;
+      }
+      if (tid == 0)
+        __hip_atomic_store(S.ticket + slot_sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // s_last is rewritten by the next item
   }
-}
-
-// Split mode only: fold the chunk states of every sequence that spans several
-// work items, in chunk order (one 64-thread workgroup per sequence).
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p) {
-  const int nseq = p.NL * p.B * p.H;
-  int sid = blockIdx.x;
-  const AttnSeg& S = sid >= nseq ? p.seg[1] : p.seg[0];
-  if (sid >= nseq) sid -= nseq;
-  const int b = (sid / p.H) % p.B;
-  int n = S.len[b];
-  n = n < 0 ? 0 : (n > S.L_cap ? S.L_cap : n);
-  const int nck = nchunks(n);
-  if (nck <= p.cpi) return;  // written whole by the attention kernel
-  const int d = threadIdx.x;
-  const float* pp = S.part + (size_t)sid * S.nck_cap * kAttnPartStride;
-  float fm = 0.f, fl = 0.f, fa = 0.f;
-  for (int c = 0; c < nck; ++c) {
-    const float* q = pp + (size_t)c * kAttnPartStride;
-    fold_chunk(c == 0, q[0], q[1], q[4 + d], fm, fl, fa);
-  }
-  S.out[(size_t)sid * kAttnHeadDim + d] = fa / fl;
 }
 
 long long attn_items_cap(const AttnParams& p) {
@@ -547,16 +559,7 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
   } else {
     hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(blocks), dim3(kAttnThreads), lds, stream, p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  bool split = false;
-  for (int s = 0; s < p.nseg; ++s) split = split || p.seg[s].nck_cap > p.cpi;
-  if (split) {
-    const int nseq = p.NL * p.B * p.H * p.nseg;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(nseq), dim3(64), 0, stream, p);
-    e = hipGetLastError();
-  }
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace dec

@@ -26,8 +26,8 @@ constexpr int kAttnPartStride = 68;                 // floats per chunk partial:
 constexpr int kAttnHeadDim = 64;
 constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
 constexpr int kAttnSortMax = 1024;                  // groups ordered longest-first up to this count
-constexpr int kAttnSplitBelow = 512;                // split sequences across workgroups below this
-                                                    // many sequences per launch
+constexpr int kAttnSplitBelow = 512;                // below this many sequences per launch, every
+                                                    // chunk is its own work item (balance)
 
 // One attention problem ("segment"): self-attention or cross-attention of a step.
 struct AttnSeg {
@@ -37,6 +37,7 @@ struct AttnSeg {
   const int32_t* len;     // [B] valid slots
   float* out;             // [NL, B, H, 64]
   float* part;            // [NL*B*H, nck_cap, kAttnPartStride] chunk partials (split mode)
+  int32_t* ticket;        // [NL*B*H] chunk arrival counters (split mode), zero between calls
   int L_cap;
   int nck_cap;            // ceil(L_cap / kAttnChunk)
 };
@@ -51,8 +52,7 @@ struct AttnParams {
 
 // Upper bound on the work items of a launch (every sequence at full capacity).
 long long attn_items_cap(const AttnParams& p);
-// Enqueue the attention kernel (and, in split mode, the chunk combine kernel);
-// `blocks` <= 0 picks the occupancy-sized persistent grid.
+// Enqueue the attention kernel; `blocks` <= 0 picks the occupancy-sized persistent grid.
 hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream);
 
 // ---- sampler ---------------------------------------------------------------------

@@ -21,11 +21,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Workspace of one attention segment: the chunk partials used when a launch
-// spreads the chunks of a sequence over several workgroups.  Capacities that fit
-// one chunk need none.
+// Workspace of one attention segment, used when a launch spreads the chunks of a
+// sequence over several workgroups: per-sequence arrival tickets (zero between
+// calls), then the chunk states.  Capacities that fit one chunk need none.
 struct SegLayout {
-  size_t bytes = 0;
+  size_t ticket_off = 0, part_off = 0, bytes = 0;
   int nck_cap = 0;
 };
 
@@ -35,7 +35,9 @@ SegLayout seg_layout(int NL, int B, int H, int L_cap) {
   s.nck_cap = (L_cap + dec::kAttnChunk - 1) / dec::kAttnChunk;
   if (s.nck_cap <= 1) return s;
   const size_t nseq = (size_t)NL * B * H;
-  s.bytes = align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
+  s.ticket_off = 0;
+  s.part_off = align_up(nseq * sizeof(int32_t), 256);
+  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
   return s;
 }
 
@@ -107,12 +109,16 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.out = segs[s].out;
     g.L_cap = segs[s].L_cap;
     g.nck_cap = lay[s].nck_cap;
-    if (lay[s].bytes > 0) g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+    if (lay[s].bytes > 0) {
+      char* base = static_cast<char*>(ws) + off;
+      g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
+      g.part = reinterpret_cast<float*>(base + lay[s].part_off);
+    }
     off += lay[s].bytes;
     if (lay[s].nck_cap > nck_max) nck_max = lay[s].nck_cap;
   }
-  // Few sequences: spread each sequence's chunks over workgroups (one chunk per
-  // item) so the chip fills; otherwise one workgroup owns a whole sequence.
+  // Few sequences: every chunk is its own work item, so the CUs get equal bytes;
+  // otherwise one workgroup owns a whole sequence (no cross-workgroup traffic).
   const long long seqs = (long long)NL * B * H * nseg;
   const int split = env_int("DECSTEP_ATTN_SPLIT", seqs < dec::kAttnSplitBelow ? 1 : 0);
   p.cpi = split ? 1 : nck_max;
@@ -137,7 +143,6 @@ size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_se
 }
 
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {
-  // The workspace carries no state between calls; zeroing it is optional.
   if (ws_bytes == 0) return DEC_OK;
   if (workspace == nullptr) return DEC_E_NULL;
   if (!aligned(workspace, 16)) return DEC_E_ALIGN;

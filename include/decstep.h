@@ -64,16 +64,17 @@ int dec_attn_chunk_keys(void);
 
 /* Workspace bytes for attention over n_layers x B x H sequences with a self
  * cache of L_cap_self slots and a cross cache of L_cap_cross slots (pass 0 for
- * a cache that the call does not use).  The workspace holds chunk partials when
- * a launch spreads a sequence over several workgroups (launches with few
- * sequences do); capacities that fit one chunk need none.  One workspace sized
- * for both caches serves dec_attn_self, dec_attn_cross and dec_attn_step.
- * Returns 0 on bad sizes. */
+ * a cache that the call does not use).  It holds, per sequence, an arrival
+ * counter and the chunk states used when a launch spreads a sequence's chunks
+ * over several workgroups (launches with few sequences do); capacities that fit
+ * one chunk need none.  One workspace sized for both caches serves
+ * dec_attn_self, dec_attn_cross and dec_attn_step.  Returns 0 on bad sizes. */
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,
                                 int L_cap_self, int L_cap_cross);
 
-/* Zero a workspace with a fill kernel (capturable).  Optional: the attention
- * calls keep no state in the workspace between calls.  Calls that share one
+/* Zero a workspace with a fill kernel (capturable).  Required once after
+ * allocation: the arrival counters must start at zero, and every attention
+ * call leaves them at zero again when it completes.  Calls that share one
  * workspace must be ordered (same stream); concurrent use of one workspace
  * races. */
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream);
