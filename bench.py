@@ -35,7 +35,68 @@ def parse(argv=None):
                     help="event-timed attention launches for the roofline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="run warmup + steps eager steps (no graph, no timing) and exit;\n"
+                         "the launch sequence the hardware-counter runs profile")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB five times and exit;\n"
+                         "the calibration for the HBM byte counters")
     return ap.parse_args(argv)
+
+
+KERNEL_SOURCES = ("attn_decode.hip", "dec_kernels.h", "dec_common.h")
+
+
+def kernel_sources_sha256():
+    """Hash of the attention kernel's sources: counter readings taken on other
+    sources no longer describe the kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "autoregressive_audio_token_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary of this
+    workload (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy calibration),
+    or None with the reason when there is none or the kernel changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"attn_decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-json: "):
+                rec = json.loads(line[len("traffic-json: "):])
+    if rec is None:
+        return None, "counter summary has no traffic-json line"
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    return rec, "counters match the current kernel sources"
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy (bitwise NOT of int32, read n bytes, write n
+    bytes) whose FETCH_SIZE / WRITE_SIZE readings scale the attention's."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.bitwise_not(a, out=b)
+    torch.cuda.synchronize()
+    ok = bool((b[:: max(1, n // 4096)] == -2).all().item())
+    print(json.dumps({"mode": "copy-calibration", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": 5,
+                      "kernel": "torch bitwise_not int32 (elementwise)", "ok": ok}), flush=True)
+    return 0 if ok else 1
 
 
 def cpu_baseline(w, seconds):
@@ -94,6 +155,8 @@ def main(argv=None):
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has "
               "no multi-GPU path: every GPU box here has a single MI355X.", file=sys.stderr)
         return 2
+    if a.copy_mib > 0:
+        return copy_calibration(a.copy_mib)
 
     import numpy as np
     import torch
@@ -137,6 +200,18 @@ def main(argv=None):
                             None, None, s)
 
     torch.cuda.synchronize()
+    if a.eager:
+        with torch.cuda.stream(stream):
+            dec.dec_attn_workspace_init(ws, nb, stream)
+            for i in range(a.warmup + a.steps):
+                attn(sets[i % R], stream)
+                sample(stream)
+        stream.synchronize()
+        print(json.dumps({"mode": "eager", "workload": w.name, "steps": a.warmup + a.steps,
+                          "cache_sets": R, "valid_kv_bytes_per_step": valid,
+                          "outputs_finite": bool(torch.isfinite(o_s).all().item())}),
+              flush=True)
+        return 0
     with torch.cuda.stream(stream):
         dec.dec_attn_workspace_init(ws, nb, stream)
         for st in sets:                  # eager warm-up of every set
@@ -205,6 +280,7 @@ def main(argv=None):
     pair_us = sum(per) / len(per)
     achieved = valid / (k_us * 1e-6) / 1e9
     dec.dec_graph_destroy(graph)
+    traffic_rec, traffic_why = counter_traffic(w.name)
 
     result = {
         "metric": METRIC,
@@ -234,7 +310,11 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm", "kernel": "attn_decode_kernel (dec_attn_step)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None,
+            "traffic_detail": {"status": traffic_why, **({k: traffic_rec[k] for k in (
+                "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch", "fetch_scale",
+                "write_scale", "ratio_to_algorithmic")} if traffic_rec else {})},
             "avg_launch_us": round(k_us, 3),
             "avg_launch_us_method": f"HIP events around a captured graph of {n_k} launches, "
                                     f"{k_reps} replays",

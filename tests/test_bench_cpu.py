@@ -1,0 +1,44 @@
+"""Host-side pieces of bench.py: the one-GPU guard and the counter-traffic record."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_counter_record_parses_and_is_consistent():
+    rec, why = bench.counter_traffic("long_description")
+    if rec is None:
+        # the summary exists; only a kernel change may disable it
+        assert why == "kernel sources changed since the counters were taken"
+        path = os.path.join(ROOT, "profiles", "attn_decode_long_description_counters.md")
+        line = [ln for ln in open(path) if ln.startswith("traffic-json: ")][-1]
+        rec = json.loads(line[len("traffic-json: "):])
+    # scaled counters add up, and each scale is what the copy calibration gives
+    kib = 1024
+    assert abs(rec["fetch_scale"] - rec["copy_calibration_bytes"]
+               / (rec["copy_fetch_size_kib"] * kib)) < 1e-4
+    assert abs(rec["write_scale"] - rec["copy_calibration_bytes"]
+               / (rec["copy_write_size_kib"] * kib)) < 1e-4
+    rd = rec["fetch_size_kib_per_dispatch"] * kib * rec["fetch_scale"]
+    wr = rec["write_size_kib_per_dispatch"] * kib * rec["write_scale"]
+    assert abs(rec["hbm_read_bytes_per_launch"] - rd) / rd < 1e-4
+    assert abs(rec["hbm_write_bytes_per_launch"] - wr) < 1
+    assert rec["hbm_bytes_per_launch"] == (rec["hbm_read_bytes_per_launch"]
+                                           + rec["hbm_write_bytes_per_launch"])
+
+
+def test_unknown_workload_has_no_traffic():
+    rec, why = bench.counter_traffic("no_such_workload")
+    assert rec is None and "no counter summary" in why
