@@ -18,7 +18,10 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 #define DEC_ATTN_TILE_KEYS 64
 #endif
 constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile
-constexpr int kAttnChunk = 1024;                    // keys per chunk
+#ifndef DEC_ATTN_CHUNK
+#define DEC_ATTN_CHUNK 1024
+#endif
+constexpr int kAttnChunk = DEC_ATTN_CHUNK;          // keys per chunk
 constexpr int kAttnTilesPerChunk = kAttnChunk / (kAttnWaves * kAttnKeysPerTile);
 static_assert(kAttnTilesPerChunk * kAttnWaves * kAttnKeysPerTile == kAttnChunk,
               "a chunk is a whole number of workgroup tile rounds");

@@ -34,49 +34,101 @@
 
 namespace dec {
 
-constexpr int kSurvSlots = 3;  // survivor slots per lane after pruning
+constexpr int kSurvSlots = 3;                   // survivor slots per lane after pruning
+constexpr int kSurvCap = kSurvSlots * kWave;     // survivors that fit
 
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0u));
 }
 
-// Exact top-kk over NS slots per lane, slot-major order = vocabulary order.
-// Absent slots carry key 0 and ok = false.  Writes the kept (value, index)
-// pairs, in order, to cval/cidx[0..kk).
+// Inverse of order_key (-0 comes back as +0; NaN payloads survive).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Largest key in the wave: DPP within 16-lane rows, then the four row results.
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  auto step = [](uint32_t x, int y) { const uint32_t u = static_cast<uint32_t>(y); return x > u ? x : u; };
+  v = step(v, __builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = step(v, __builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, false));
+  v = step(v, __builtin_amdgcn_update_dpp(0, (int)v, kDppHalfMirror, 0xF, 0xF, false));
+  v = step(v, __builtin_amdgcn_update_dpp(0, (int)v, kDppRowMirror, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// Count of keys >= t over NS slots, across the wave.
 template <int NS>
-__device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const float (&val)[NS],
-                                            const int (&idx)[NS], int kk, float* cval,
-                                            int* cidx) {
-  // the largest t with #(key >= t) >= kk, i.e. the kk-th largest key; stop early
-  // once exactly kk keys are >= t
-  uint32_t tau = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int cnt = 0;
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[NS], uint32_t t) {
+  int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-    if (cnt >= kk) {
-      tau = cand;
-      if (cnt == kk) break;
+  for (int j = 0; j < NS; ++j) cnt += __popcll(__ballot(key[j] >= t));
+  return cnt;
+}
+
+// Search step over two bits below `bit` + 1 of tau: the three candidates are
+// counted independently, so a step costs one dependency chain for two bits.
+// Keeps the invariant #(key >= tau) >= kk; returns true once exactly kk keys are >= tau.
+template <int NS>
+__device__ __forceinline__ bool search2(const uint32_t (&key)[NS], int kk, int lowbit, uint32_t& tau) {
+  const uint32_t c1 = tau | (1u << lowbit), c2 = tau | (2u << lowbit), c3 = tau | (3u << lowbit);
+  const int n1 = count_ge(key, c1), n2 = count_ge(key, c2), n3 = count_ge(key, c3);
+  if (n3 >= kk) { tau = c3; return n3 == kk; }
+  if (n2 >= kk) { tau = c2; return n2 == kk; }
+  if (n1 >= kk) { tau = c1; return n1 == kk; }
+  return false;
+}
+
+// Exact top-kk over NS slots per lane whose slot-major order is vocabulary order.
+// Absent slots carry key 0 and idx -1.  Every present key is at least `lo`, and
+// the largest is `hi`, so the search starts below their common leading bits.
+// Writes the kept (value, index) pairs in vocabulary order to cval/cidx[0..kk)
+// (lanes outside the kept set write a dummy slot, so no store is predicated).
+template <int NS>
+__device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const int (&idx)[NS], int kk,
+                                            uint32_t lo, uint32_t hi, float* cval, int* cidx) {
+  // tau: the largest t with #(key >= t) >= kk (the kk-th largest key), or the
+  // first t at which exactly kk keys are >= t; both give the same kept set
+  const uint32_t diff = lo ^ hi;
+  uint32_t tau = hi;
+  if (diff != 0u) {
+    const int top = 31 - __builtin_clz(diff);
+    tau = top == 31 ? 0u : (hi & ~((2u << top) - 1u));  // the shared leading bits
+    int bit = top;
+    bool done = false;
+    if ((bit & 1) == 0) {  // an odd number of bits to resolve: one single-bit step first
+      const uint32_t cand = tau | (1u << bit);
+      const int cnt = count_ge(key, cand);
+      if (cnt >= kk) {
+        tau = cand;
+        done = cnt == kk;
+      }
+      --bit;
     }
+    for (; !done && bit > 0; bit -= 2) done = search2(key, kk, bit - 1, tau);
   }
   int cnt_gt = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
   const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
   int eq_before = 0, kept_before = 0;
+  const int lane = static_cast<int>(__lane_id());
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const bool eq = idx[j] >= 0 && key[j] == tau;
     const unsigned long long eqm = __ballot(eq);
     const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
     const unsigned long long km = __ballot(kept);
-    if (kept) {
-      const int pos = kept_before + lanes_below(km);
-      cval[pos] = val[j];
-      cidx[pos] = idx[j];
-    }
+    const int pos = kept ? kept_before + lanes_below(km) : kWave + lane;
+    cval[pos] = key_value(key[j]);
+    cidx[pos] = idx[j];
     eq_before += __popcll(eqm);
     kept_before += __popcll(km);
   }
@@ -84,114 +136,114 @@ __device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const flo
 
 template <int VPL>
 __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
-  __shared__ float s_val[kSampWaves][kWave];
-  __shared__ int s_idx[kSampWaves][kWave];
-  __shared__ uint32_t s_skey[kSampWaves][kSurvSlots * kWave];
-  __shared__ float s_sval[kSampWaves][kSurvSlots * kWave];
-  __shared__ int s_sidx[kSampWaves][kSurvSlots * kWave];
+  // per wave: kept entries [0, 64) plus one dummy slot per lane; survivors
+  // [0, kSurvCap) plus one dummy slot per lane
+  __shared__ float s_val[kSampWaves][2 * kWave];
+  __shared__ int s_idx[kSampWaves][2 * kWave];
+  __shared__ uint2 s_surv[kSampWaves][kSurvCap + kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int rows = p.B * p.n_cb;
   const int row = blockIdx.x * kSampWaves + wave;
-  const bool active = row < rows;  // uniform per wave; inactive waves still reach the barrier
+  if (row >= rows) return;  // uniform per wave; waves never wait on each other
   const int kk = p.top_k < p.V_valid ? p.top_k : p.V_valid;
 
   // per-row scalars first, so their latency overlaps the logits' and the selection
-  const int b = active ? row / p.n_cb : 0;
-  const int c = active ? row - b * p.n_cb : 0;
-  const float T = active ? p.temperature[b] : 1.f;
-  const float u = active ? p.uniforms[row] : 0.f;
-  const int started = (active && p.step != nullptr) ? (p.step[b] >= c) : 1;
+  const int b = row / p.n_cb;
+  const int c = row - b * p.n_cb;
+  const float T = p.temperature[b];
+  const float u = p.uniforms[row];
+  const int started = p.step != nullptr ? (p.step[b] >= c) : 1;
 
-  if (active) {
-    const float* x = p.logits + (size_t)row * p.V_stride;
-    float v[VPL];
-    uint32_t key[VPL];
-    int idx[VPL];
+  const float* x = p.logits + (size_t)row * p.V_stride;
+  float v[VPL];
+  uint32_t key[VPL];
+  int idx[VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
-      const int i = j * kWave + lane;
-      v[j] = x[i < p.V_valid ? i : p.V_valid - 1];
-    }
-    uint32_t lmax = 0u;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int i = j * kWave + lane;
-      const bool ok = i < p.V_valid;
-      key[j] = ok ? order_key(v[j]) : 0u;  // absent entries: below every candidate
-      idx[j] = ok ? i : -1;
-      lmax = key[j] > lmax ? key[j] : lmax;
-    }
-    // L0: the kk-th largest lane maximum, to its 10 leading bits (a lower bound either way)
-    uint32_t l0 = 0u;
-    for (int bit = 31; bit >= 22; --bit) {
-      const uint32_t cand = l0 | (1u << bit);
-      if (__popcll(__ballot(lmax >= cand)) >= kk) l0 = cand;
-    }
-    // compact the survivors in vocabulary order (as long as they fit)
-    int nsurv = 0;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const bool sv = idx[j] >= 0 && key[j] >= l0;
-      const unsigned long long m = __ballot(sv);
-      const int pos = nsurv + lanes_below(m);
-      if (sv && pos < kSurvSlots * kWave) {
-        s_skey[wave][pos] = key[j];
-        s_sval[wave][pos] = v[j];
-        s_sidx[wave][pos] = idx[j];
-      }
-      nsurv += __popcll(m);
-    }
-    if (nsurv <= kSurvSlots * kWave) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      uint32_t sk[kSurvSlots];
-      float sv[kSurvSlots];
-      int si[kSurvSlots];
-#pragma unroll
-      for (int j = 0; j < kSurvSlots; ++j) {
-        const int q = j * kWave + lane;
-        const bool ok = q < nsurv;
-        sk[j] = ok ? s_skey[wave][q] : 0u;
-        sv[j] = ok ? s_sval[wave][q] : 0.f;
-        si[j] = ok ? s_sidx[wave][q] : -1;
-      }
-      select_kept(sk, sv, si, kk, s_val[wave], s_idx[wave]);
-    } else {  // too many survivors (heavy ties or a flat row): search the whole row
-      select_kept(key, v, idx, kk, s_val[wave], s_idx[wave]);
-    }
+  for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
+    const int i = j * kWave + lane;
+    v[j] = x[i < p.V_valid ? i : p.V_valid - 1];
   }
-  __syncthreads();
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int i = j * kWave + lane;
+    const bool ok = i < p.V_valid;
+    key[j] = order_key(v[j]) & (ok ? 0xFFFFFFFFu : 0u);  // absent: below every candidate
+    idx[j] = ok ? i : -1;
+    lmax = key[j] > lmax ? key[j] : lmax;
+  }
+  const uint32_t kmax = wave_max_key(lmax);
+  // L0: the kk-th largest lane maximum, to its 10 leading bits (a lower bound on
+  // the kk-th largest key either way: at least kk lanes hold a key >= L0)
+  uint32_t l0 = 0u;
+  {
+    const uint32_t lm[1] = {lmax};
+    for (int bit = 31; bit > 22; bit -= 2) (void)search2(lm, kk, bit - 1, l0);
+  }
+  // compact the survivors (key >= L0) in vocabulary order, as long as they fit;
+  // absent entries have key 0, so a threshold of at least 1 leaves them out
+  const uint32_t thr = uniform(l0 > 1u ? l0 : 1u);
+  uint2* surv = s_surv[wave];
+  int nsurv = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const bool sv = key[j] >= thr;
+    const unsigned long long m = __ballot(sv);
+    const int pos = nsurv + lanes_below(m);
+    // past the capacity (the full-row search is taken then) or not a survivor:
+    // a dummy slot, never read
+    const int dummy = kSurvCap + lane;
+    surv[sv ? min(pos, dummy) : dummy] = make_uint2(key[j], (uint32_t)idx[j]);
+    nsurv += __popcll(m);
+  }
+  if (nsurv >= kk && nsurv <= kSurvCap) {  // (fewer than kk only if L0 found nothing)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t sk[kSurvSlots];
+    int si[kSurvSlots];
+#pragma unroll
+    for (int j = 0; j < kSurvSlots; ++j) {
+      const int q = j * kWave + lane;
+      const uint2 e = surv[q < nsurv ? q : kSurvCap + lane];
+      sk[j] = q < nsurv ? e.x : 0u;
+      si[j] = q < nsurv ? (int)e.y : -1;
+    }
+    select_kept(sk, si, kk, thr, kmax, s_val[wave], s_idx[wave]);
+  } else {  // too many survivors (heavy ties or a flat row): search the whole row
+    select_kept(key, idx, kk, 0u, kmax, s_val[wave], s_idx[wave]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  if (active) {
-    const bool act = lane < kk;
-    const float xv = act ? s_val[wave][lane] : -INFINITY;
-    const int xi = act ? s_idx[wave][lane] : -1;
-    const float m = wave_max(xv);
-    int sel;
-    float prob;
-    if (T <= 0.f) {
-      const unsigned long long mk = __ballot(act && xv == m);
-      sel = mk ? __ffsll(mk) - 1 : 0;
-      prob = lane == sel ? 1.f : 0.f;
-    } else {
-      const float e = act ? expf((xv - m) / T) : 0.f;
-      const float S = wave_inclusive_sum(e, lane);
-      const float Z = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kk - 1));
-      const float C = S / Z;
-      const unsigned long long mk = __ballot(act && u < C);
-      sel = mk ? __ffsll(mk) - 1 : kk - 1;
-      prob = e / Z;
-    }
-    int token = __builtin_amdgcn_readlane(xi, sel);
-    if (!started) token = p.fill;
-    if (lane == 0) p.tokens[row] = token;
-    if (lane < p.top_k) {
-      if (p.topk_idx != nullptr) p.topk_idx[(size_t)row * p.top_k + lane] = act ? xi : -1;
-      if (p.topk_prob != nullptr) p.topk_prob[(size_t)row * p.top_k + lane] = act ? prob : 0.f;
-    }
+  const bool act = lane < kk;
+  const float xv = act ? s_val[wave][lane] : -INFINITY;
+  const int xi = act ? s_idx[wave][lane] : -1;
+  const float m = key_value(kmax);  // the row maximum is always kept
+  int sel;
+  float prob;
+  if (T <= 0.f) {
+    const unsigned long long mk = __ballot(act && xv == m);
+    sel = mk ? __ffsll(mk) - 1 : 0;
+    prob = lane == sel ? 1.f : 0.f;
+  } else {
+    const float e = act ? expf((xv - m) / T) : 0.f;
+    const float S = wave_inclusive_sum(e, lane);
+    const float Z = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kk - 1));
+    const float C = S / Z;
+    const unsigned long long mk = __ballot(act && u < C);
+    sel = mk ? __ffsll(mk) - 1 : kk - 1;
+    prob = e / Z;
+  }
+  int token = __builtin_amdgcn_readlane(xi, sel);
+  if (!started) token = p.fill;
+  if (lane == 0) p.tokens[row] = token;
+  if (lane < p.top_k) {
+    if (p.topk_idx != nullptr) p.topk_idx[(size_t)row * p.top_k + lane] = act ? xi : -1;
+    if (p.topk_prob != nullptr) p.topk_prob[(size_t)row * p.top_k + lane] = act ? prob : 0.f;
   }
 }
 
