@@ -265,37 +265,33 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   int* s_pref = s_dyn + 2 * G;
 
   // ---- item list: groups (segment, b) longest first; group_items(n) each -------------
-  if (G <= kWave) {
-    // One group per lane of wave 0; the other waves go straight to the barrier.
-    if (wave == 0) {
-      int n = 0, items = 0;
-      if (lane < G) {
-        const bool cross = lane >= B;
-        const int32_t* len = cross ? p.seg[1].len : p.seg[0].len;
-        const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
-        n = len[cross ? lane - B : lane];
-        n = n < 0 ? 0 : (n > cap ? cap : n);
-        items = group_items(n, NLH, cpi);
-      }
-      int rank = 0;  // stable rank by descending length
-      for (int j = 0; j < G; ++j) {
-        const int nj = __builtin_amdgcn_readlane(n, j);
-        rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
-      }
-      if (lane < G) {
-        s_n[lane] = n;
-        s_order[rank] = lane;
-        s_pref[rank + 1] = items;  // scanned in place below
-      }
-      if (lane == 0) s_pref[0] = 0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int v = lane < G ? s_pref[lane + 1] : 0;
-      const int incl = wave_inclusive_sum_int(v, lane);
-      if (lane < G) s_pref[lane + 1] = incl;
+  // Up to 64 groups: every wave derives the list in registers (lane r holds the group of
+  // rank r and the inclusive item prefix), so no wave waits on another.  More groups:
+  // the list is built in LDS and searched.
+  const bool in_regs = G <= kWave;
+  int r_n = 0, r_order = 0, r_items = 0, r_incl = 0, total = 0;
+  if (in_regs) {
+    int n = 0, items = 0;
+    if (lane < G) {
+      const bool cross = lane >= B;
+      const int32_t* len = cross ? p.seg[1].len : p.seg[0].len;
+      const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
+      n = len[cross ? lane - B : lane];
+      n = n < 0 ? 0 : (n > cap ? cap : n);
+      items = group_items(n, NLH, cpi);
     }
-    __syncthreads();
+    int rank = 0;  // stable rank by descending length
+    for (int j = 0; j < G; ++j) {
+      const int nj = __builtin_amdgcn_readlane(n, j);
+      rank += (nj > n || (nj == n && j < lane)) ? 1 : 0;
+    }
+    // lane `rank` receives the group and its item count (a permutation of lanes < G)
+    const int dst = (lane < G ? rank : lane) * 4;
+    r_n = n;
+    r_order = __builtin_amdgcn_ds_permute(dst, lane);
+    r_items = __builtin_amdgcn_ds_permute(dst, items);
+    r_incl = wave_inclusive_sum_int(lane < G ? r_items : 0, lane);
+    total = __builtin_amdgcn_readlane(r_incl, G - 1);
   } else {
     for (int g = tid; g < G; g += kAttnThreads) {
       const bool cross = g >= B;
@@ -326,7 +322,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     int ex = wave_inclusive_sum_int(local, lane) - local;
     if (lane == kWave - 1) s_wsum[wave] = ex + local;
     __syncthreads();
-    int total = 0;
     for (int w = 0; w < kAttnWaves; ++w) {
       if (w < wave) ex += s_wsum[w];
       total += s_wsum[w];
@@ -338,24 +333,31 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     if (tid == 0) s_pref[G] = total;
     __syncthreads();
   }
-  const int total = s_pref[G];
 
   const int kg = lane / LPK;  // key slot within a wave-wide load (lane group)
   const int dl = lane % LPK;  // which 16-byte slice of the row this lane reads
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // locate the group: the largest position with s_pref[pos] <= item
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
+    // locate the group of this item and the item's index within the group
+    int g, n, r;
+    if (in_regs) {  // sorted position: the number of groups whose items end at or before it
+      const int pos = __popcll(__ballot(lane < G && r_incl <= item));
+      g = __builtin_amdgcn_readlane(r_order, pos);
+      r = item - (__builtin_amdgcn_readlane(r_incl, pos) - __builtin_amdgcn_readlane(r_items, pos));
+      n = __builtin_amdgcn_readlane(r_n, g);
+    } else {  // the largest position with s_pref[pos] <= item
+      int lo = 0, hi = G - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      g = s_order[lo];
+      n = s_n[g];
+      r = item - s_pref[lo];
     }
-    const int g = s_order[lo];
     const bool cross = g >= B;
     const AttnSeg& S = cross ? p.seg[1] : p.seg[0];
     const int b = cross ? g - B : g;
-    const int n = s_n[g];
-    const int r = item - s_pref[lo];
     const int nck = nchunks(n);
     const int spw = waves_per_seq(n);            // waves per sequence
     const bool packed = spw < kAttnWaves;        // several sequences share this item
