@@ -22,9 +22,14 @@ Source: the "Optimized Parler TTS" page.
   * delay.py      -- the delayed codebook pattern: 9 tokens per step, codebook
     c lagging c steps ("A rough architecture of Parler TTS", the delay-pattern
     figure taken from the MusicGen paper).
+  * cache.py      -- writing the current token's key/value row into the
+    preallocated cache ("Analysis and improvements": static caches).
+  * rng.py        -- counter-based uniforms (Philox4x64-10 from its published
+    definition), so sampling needs no random numbers from the host
+    ("Analysis and improvements": sampling without a GPU/CPU synchronisation).
 
 Every function here is pinned by a CPU test against something other than
 itself (closed forms, library routines, brute force, invariants); none is
 "parity unpinned".
 """
-from . import attn, sampling, delay  # noqa: F401
+from . import attn, sampling, delay, cache, rng  # noqa: F401
