@@ -2,8 +2,21 @@
 on AMD Instinct MI355X (gfx950).
 
 The compute lives in libdecstep.so (HIP kernels behind a C ABI, declared in
-include/decstep.h); ``decstep`` is its thin ctypes binding.  Importing this
-package loads the library and fails if it has not been built.
+include/decstep.h); ``decstep`` is its thin ctypes binding.  The binding (and
+with it the library) loads on first use of any of its names, so the ``build``
+module can run before the library exists; that first use fails with an
+ImportError if the library has not been built.
 """
-from . import decstep  # noqa: F401
-from .decstep import *  # noqa: F401,F403
+import importlib
+
+
+def __getattr__(name):
+    if name.startswith("__"):
+        raise AttributeError(name)
+    mod = importlib.import_module(__name__ + ".decstep")
+    if name == "decstep":
+        return mod
+    try:
+        return getattr(mod, name)
+    except AttributeError:
+        raise AttributeError(f"module {__name__!r} has no attribute {name!r}") from None

@@ -66,12 +66,14 @@ constexpr int kSampMaxVocab = 4096;
 struct SampleParams {
   const float* logits;
   const float* temperature;
-  const float* uniforms;
+  const float* uniforms;  // [B, n_cb], or unused when rng != 0
   const int32_t* step;
   int32_t* tokens;
   int32_t* topk_idx;
   float* topk_prob;
+  unsigned long long seed;  // Philox key word 0 when rng != 0
   int B, n_cb, V_valid, V_stride, top_k, fill;
+  int rng;                  // 1: uniforms from Philox4x64-10 at counter (step, b, c, 0)
 };
 
 hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
@@ -79,6 +81,20 @@ hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
 // ---- small utility kernels ------------------------------------------------------------
 
 hipError_t fill_zero_launch(void* ptr, size_t bytes, hipStream_t stream);
+
+// ---- cache append: the current token's K/V rows into slot len[b] - 1 --------------------
+
+struct AppendParams {
+  const void* k_new;      // [NL, B, H, row_bytes]
+  const void* v_new;
+  void* k_cache;          // [NL, B, H, L_cap, row_bytes]
+  void* v_cache;
+  const int32_t* len;     // [B]
+  int NL, B, H, L_cap;
+  int row16;              // 16-byte pieces per row
+};
+
+hipError_t append_launch(const AppendParams& p, hipStream_t stream);
 hipError_t advance_launch(int32_t* len, int32_t* step, int B, hipStream_t stream);
 
 }  // namespace dec

@@ -208,6 +208,66 @@ int dec_sample_topk(const float* logits, int B, int n_cb, int V_valid, int V_str
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
+int dec_sample_topk_philox(const float* logits, int B, int n_cb, int V_valid, int V_stride,
+                           const float* temperature, int top_k, uint64_t seed,
+                           const int32_t* step, int32_t fill_token, int32_t* tokens,
+                           int32_t* topk_idx, float* topk_prob, dec_stream_t stream) {
+  if (!logits || !temperature || !tokens) return DEC_E_NULL;
+  if (B < 1 || n_cb < 1 || V_valid < 1 || V_stride < V_valid) return DEC_E_SHAPE;
+  if ((long long)B * n_cb > (1LL << 30) || (long long)B * n_cb * V_stride > (1LL << 46))
+    return DEC_E_SHAPE;
+  if (top_k < 1 || top_k > 64) return DEC_E_SHAPE;
+  if (V_valid > dec::kSampMaxVocab) return DEC_E_UNSUPPORTED;
+  if (!aligned(logits, 4) || !aligned(temperature, 4) || !aligned(step, 4) ||
+      !aligned(tokens, 4) || !aligned(topk_idx, 4) || !aligned(topk_prob, 4))
+    return DEC_E_ALIGN;
+  dec::SampleParams p{};
+  p.logits = logits;
+  p.temperature = temperature;
+  p.uniforms = nullptr;
+  p.step = step;
+  p.tokens = tokens;
+  p.topk_idx = topk_idx;
+  p.topk_prob = topk_prob;
+  p.seed = seed;
+  p.rng = 1;
+  p.B = B;
+  p.n_cb = n_cb;
+  p.V_valid = V_valid;
+  p.V_stride = V_stride;
+  p.top_k = top_k;
+  p.fill = fill_token;
+  const hipError_t e = dec::sample_launch(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* len, int n_layers, int B, int H, int L_cap, int hd, int dtype,
+                  dec_stream_t stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !len) return DEC_E_NULL;
+  if (dtype != DEC_BF16 && dtype != DEC_F32) return DEC_E_DTYPE;
+  if (n_layers < 1 || B < 1 || H < 1 || L_cap < 1 || hd < 1) return DEC_E_SHAPE;
+  const long long row_bytes = (long long)hd * (dtype == DEC_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0) return DEC_E_UNSUPPORTED;
+  if ((long long)n_layers * B * H * L_cap * row_bytes > (1LL << 46)) return DEC_E_SHAPE;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(len, 4))
+    return DEC_E_ALIGN;
+  dec::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.len = len;
+  p.NL = n_layers;
+  p.B = B;
+  p.H = H;
+  p.L_cap = L_cap;
+  p.row16 = (int)(row_bytes / 16);
+  const hipError_t e = dec::append_launch(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream) {
   if (B < 1) return DEC_E_SHAPE;
   if (len == nullptr && step == nullptr) return DEC_E_NULL;

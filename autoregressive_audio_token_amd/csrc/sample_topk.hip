@@ -134,6 +134,27 @@ __device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const int
   }
 }
 
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011); returns output word 0 for counter c and key k.
+__device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                     uint64_t c3, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kMulA = 0xD2E7470EE14C6C93ull, kMulB = 0xCA5A826395121157ull;
+  constexpr uint64_t kWeylA = 0x9E3779B97F4A7C15ull, kWeylB = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t ha = __umul64hi(kMulA, c0), la = kMulA * c0;
+    const uint64_t hb = __umul64hi(kMulB, c2), lb = kMulB * c2;
+    const uint64_t n0 = hb ^ c1 ^ k0, n2 = ha ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lb;
+    c2 = n2;
+    c3 = la;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  return c0;
+}
+
 template <int VPL>
 __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
   // per wave: kept entries [0, 64) plus one dummy slot per lane; survivors
@@ -153,8 +174,16 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   const int b = row / p.n_cb;
   const int c = row - b * p.n_cb;
   const float T = p.temperature[b];
-  const float u = p.uniforms[row];
-  const int started = p.step != nullptr ? (p.step[b] >= c) : 1;
+  const int st = p.step != nullptr ? p.step[b] : 0;
+  const int started = p.step != nullptr ? (st >= c) : 1;
+  float u;
+  if (p.rng) {  // counter (step, b, c, 0), key (seed, 0): top 24 bits of word 0
+    const uint64_t w = philox4x64_10_w0((uint64_t)(int64_t)st, (uint64_t)b, (uint64_t)c, 0ull,
+                                        p.seed, 0ull);
+    u = (float)(uint32_t)(w >> 40) * 0x1p-24f;
+  } else {
+    u = p.uniforms[row];
+  }
 
   const float* x = p.logits + (size_t)row * p.V_stride;
   float v[VPL];
@@ -289,6 +318,34 @@ __global__ void advance_kernel(int32_t* len, int32_t* step, int B) {
     if (len != nullptr) len[b] += 1;
     if (step != nullptr) step[b] += 1;
   }
+}
+
+__global__ void append_kernel(AppendParams p) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const long long rows = (long long)p.NL * p.B * p.H;
+  const long long n = rows * p.row16;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long row = i / p.row16;
+    const int piece = (int)(i - row * p.row16);
+    const int b = (int)((row / p.H) % p.B);
+    const int len = p.len[b];
+    if (len < 1 || len > p.L_cap) continue;  // nothing to write for this sequence
+    const u32x4_t* kn = static_cast<const u32x4_t*>(p.k_new) + row * p.row16 + piece;
+    const u32x4_t* vn = static_cast<const u32x4_t*>(p.v_new) + row * p.row16 + piece;
+    const long long dst = (row * p.L_cap + (len - 1)) * p.row16 + piece;
+    static_cast<u32x4_t*>(p.k_cache)[dst] = *kn;
+    static_cast<u32x4_t*>(p.v_cache)[dst] = *vn;
+  }
+}
+
+hipError_t append_launch(const AppendParams& p, hipStream_t stream) {
+  const long long n = (long long)p.NL * p.B * p.H * p.row16;
+  if (n == 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t advance_launch(int32_t* len, int32_t* step, int B, hipStream_t stream) {

@@ -55,6 +55,9 @@ _SIGS = {
                            _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_sample_topk": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _P, ctypes.c_int32, _P, _P, _P,
                              _P]),
+    "dec_sample_topk_philox": (_I, [_P, _I, _I, _I, _I, _P, _I, ctypes.c_uint64, _P,
+                                    ctypes.c_int32, _P, _P, _P, _P]),
+    "dec_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "dec_step_advance": (_I, [_P, _P, _I, _P]),
     "dec_graph_begin": (_I, [_P]),
     "dec_graph_end": (_I, [_P, ctypes.POINTER(_P)]),
@@ -152,6 +155,20 @@ def dec_sample_topk(logits, B, n_cb, V_valid, V_stride, temperature, top_k, unif
     _check(_lib.dec_sample_topk(_ptr(logits), B, n_cb, V_valid, V_stride, _ptr(temperature),
                                 top_k, _ptr(uniforms), _ptr(step), fill_token, _ptr(tokens),
                                 _ptr(topk_idx), _ptr(topk_prob), _stream(stream)))
+
+
+def dec_sample_topk_philox(logits, B, n_cb, V_valid, V_stride, temperature, top_k, seed, step,
+                           fill_token, tokens, topk_idx=None, topk_prob=None, stream=None):
+    _check(_lib.dec_sample_topk_philox(_ptr(logits), B, n_cb, V_valid, V_stride,
+                                       _ptr(temperature), top_k, seed, _ptr(step), fill_token,
+                                       _ptr(tokens), _ptr(topk_idx), _ptr(topk_prob),
+                                       _stream(stream)))
+
+
+def dec_kv_append(k_new, v_new, k_cache, v_cache, len, n_layers, B, H, L_cap, hd, dtype,
+                  stream=None):
+    _check(_lib.dec_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(len),
+                              n_layers, B, H, L_cap, hd, dtype, _stream(stream)))
 
 
 def dec_step_advance(len, step, B, stream=None):

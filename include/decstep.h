@@ -145,6 +145,38 @@ int dec_sample_topk(const float* logits, int B, int n_cb, int V_valid, int V_str
                     const int32_t* step, int32_t fill_token, int32_t* tokens,
                     int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
 
+/* As dec_sample_topk, but the uniform of row (b, c) is generated on the device
+ * instead of read, so a captured step needs no random numbers from the host
+ * ("Analysis and improvements": sampling without a GPU/CPU synchronisation).
+ * Generator: Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011) at counter
+ * (step[b], b, c, 0) and key (seed, 0); u = (word0 >> 40) * 2^-24, in [0, 1).
+ * step == NULL: counter step 0 for every row and no delay mask, so equal calls
+ * give equal tokens.  Arguments, outputs and errors otherwise as
+ * dec_sample_topk (there is no uniforms argument). */
+int dec_sample_topk_philox(const float* logits, int B, int n_cb, int V_valid, int V_stride,
+                           const float* temperature, int top_k, uint64_t seed,
+                           const int32_t* step, int32_t fill_token, int32_t* tokens,
+                           int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
+
+/* Write the current token's key and value rows into the static caches
+ * ("Analysis and improvements": caches preallocated at a fixed capacity, so a
+ * step writes the next row instead of growing a tensor).
+ *
+ *   k_new, v_new     [n_layers, B, H, hd]          dtype, read
+ *   k_cache, v_cache [n_layers, B, H, L_cap, hd]   dtype, row len[b] - 1 written
+ *   len              [B] int32, read: the length INCLUDING the current token
+ *                    (the value dec_attn_self reads afterwards)
+ * Nothing is written for a sequence with len[b] < 1 or len[b] > L_cap.  Every
+ * pointer is a device pointer owned by the caller; caches and new rows must be
+ * 16-byte aligned and hd * sizeof(element) a multiple of 16 (else
+ * DEC_E_ALIGN / DEC_E_UNSUPPORTED).  dtype: DEC_BF16 or DEC_F32.  Rows of other
+ * slots are untouched.  Typical step order: dec_kv_append, dec_attn_step,
+ * dec_sample_topk(_philox), dec_step_advance. */
+int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* len, int n_layers, int B, int H, int L_cap, int hd, int dtype,
+                  dec_stream_t stream);
+
 /* Advance device-resident decode state by one step inside a captured graph:
  * len[b] += 1 (if len != NULL) and step[b] += 1 (if step != NULL) for b < B. */
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);

@@ -42,9 +42,18 @@ def test_every_declared_symbol_is_exported():
 
 def test_missing_library_fails_loudly():
     env = dict(os.environ, DECSTEP_LIB="/nonexistent/libdecstep.so")
-    r = subprocess.run([sys.executable, "-c", "import autoregressive_audio_token_amd"],
-                       cwd=ROOT, env=env, capture_output=True, text=True)
+    code = "import autoregressive_audio_token_amd as d; d.dec_attn_chunk_keys()"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_build_module_imports_without_the_library():
+    env = dict(os.environ, DECSTEP_LIB="/nonexistent/libdecstep.so")
+    code = "import autoregressive_audio_token_amd.build as b; print(b.LIB)"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True)
+    assert r.returncode == 0 and r.stdout.strip().endswith("libdecstep.so")
 
 
 def test_strerror_names_every_status():
@@ -120,6 +129,49 @@ def test_sampler_host_validation():
     assert _samp(V=5000, S=5000) == D.DEC_E_UNSUPPORTED
     assert _samp(lg=A + 2) == D.DEC_E_ALIGN
     assert _samp(idx=A + 1) == D.DEC_E_ALIGN
+
+
+def _samp_rng(**kw):
+    a = dict(lg=A, B=1, ncb=9, V=1089, S=1096, T=A, k=50, seed=7, step=None, fill=1089, tok=A,
+             idx=None, prob=None)
+    a.update(kw)
+    return D.raw_status("dec_sample_topk_philox", a["lg"], a["B"], a["ncb"], a["V"], a["S"],
+                        a["T"], a["k"], ctypes.c_uint64(a["seed"]), a["step"], a["fill"],
+                        a["tok"], a["idx"], a["prob"], None)
+
+
+@_no_gpu
+def test_philox_sampler_host_validation():
+    assert _samp_rng(lg=None) == D.DEC_E_NULL
+    assert _samp_rng(T=None) == D.DEC_E_NULL
+    assert _samp_rng(tok=None) == D.DEC_E_NULL
+    for bad in (dict(B=0), dict(ncb=0), dict(V=0), dict(S=1000), dict(k=0), dict(k=65)):
+        assert _samp_rng(**bad) == D.DEC_E_SHAPE, bad
+    assert _samp_rng(V=5000, S=5000) == D.DEC_E_UNSUPPORTED
+    assert _samp_rng(step=A + 2) == D.DEC_E_ALIGN
+    assert _samp_rng(prob=A + 1) == D.DEC_E_ALIGN
+
+
+def _append(**kw):
+    a = dict(kn=A, vn=A, kc=A, vc=A, len=A, NL=24, B=1, H=16, L=4096, hd=64, dt=0)
+    a.update(kw)
+    return D.raw_status("dec_kv_append", a["kn"], a["vn"], a["kc"], a["vc"], a["len"], a["NL"],
+                        a["B"], a["H"], a["L"], a["hd"], a["dt"], None)
+
+
+@_no_gpu
+def test_append_host_validation():
+    for k in ("kn", "vn", "kc", "vc", "len"):
+        assert _append(**{k: None}) == D.DEC_E_NULL, k
+    assert _append(dt=7) == D.DEC_E_DTYPE
+    for bad in (dict(NL=0), dict(B=0), dict(H=0), dict(L=0), dict(hd=0)):
+        assert _append(**bad) == D.DEC_E_SHAPE, bad
+    assert _append(hd=4) == D.DEC_E_UNSUPPORTED          # 8-byte rows
+    assert _append(hd=2, dt=1) == D.DEC_E_UNSUPPORTED
+    assert _append(NL=1 << 20, H=1 << 10, L=1 << 20) == D.DEC_E_SHAPE
+    for k in ("kn", "vn", "kc", "vc"):
+        assert _append(**{k: A + 8}) == D.DEC_E_ALIGN, k
+    assert _append(len=A + 2) == D.DEC_E_ALIGN
 
 
 @_no_gpu

@@ -1,0 +1,151 @@
+"""GPU parity of the pieces that make a decode step self-driving, through the C ABI:
+
+* dec_kv_append writes the current token's rows (bit-exact against the oracle);
+* dec_sample_topk_philox draws its own uniforms: the same bars as the sampler
+  parity, and bit-identical outputs to dec_sample_topk given the oracle's uniforms
+  (so the device generator reproduces the oracle's Philox words exactly);
+* a captured step -- append, fused attention, sampling with device uniforms, advance --
+  replayed several times with no host input, each replay checked against the oracle.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import autoregressive_audio_token_amd as dec  # noqa: E402
+from oracle import attn as oattn, cache as ocache, rng as orng  # noqa: E402
+from workloads import configs, gen, device as wdev  # noqa: E402
+from tests import hip_path as hp  # noqa: E402
+from tests.test_gpu_sampler import _compare  # noqa: E402
+
+BAR = 2e-3
+
+
+def _dev(a, dtype=None):
+    return wdev.to_device(np.asarray(a), hp.DEV, dtype)
+
+
+def _bits(t):
+    """Host copy of a device tensor as raw element bits (uint16 for bf16, uint32 for fp32)."""
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def _np_bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.astype(np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("base", ["mini_v1", "tiny"])
+def test_append_writes_exactly_the_current_rows(base):
+    w = dataclasses.replace(configs.BY_NAME[base], n_layers=2, batch=6, heads=4, self_cap=96)
+    lens = [1, 96, 0, 97, 50, -3]            # first slot, last slot, none, past the end, mid, none
+    print(f"[append] {w.name} dtype={w.dtype} lens={lens}", flush=True)
+    k0 = gen.cache(w, "self", "k", [w.self_cap] * w.batch)
+    v0 = gen.cache(w, "self", "v", [w.self_cap] * w.batch)
+    kn, vn = gen.new_rows(w, "k", 0), gen.new_rows(w, "v", 0)
+    kc, vc = _dev(k0), _dev(v0)
+    dec.dec_kv_append(_dev(kn), _dev(vn), kc, vc, _dev(np.array(lens, np.int32)), w.n_layers,
+                      w.batch, w.heads, w.self_cap, 64, hp.code(w))
+    want_k, want_v = ocache.append(kn, vn, k0.copy(), v0.copy(), lens)
+    assert np.array_equal(_bits(kc), _np_bits(want_k))
+    assert np.array_equal(_bits(vc), _np_bits(want_v))
+
+
+@pytest.mark.parametrize("name", ["tiny", "long_description", "batched_mixed"])
+def test_philox_sampler_matches_oracle_and_explicit_uniforms(name):
+    w = configs.BY_NAME[name]
+    lg, T = gen.logits(w), gen.temperatures(w)
+    steps = (np.arange(w.batch, dtype=np.int64) * 7 + 1).astype(np.int32)
+    seed = 0x5EED00001234 + w.cfg_id
+    print(f"[philox] {name} B={w.batch} seed={seed:#x}", flush=True)
+    lg_d, T_d, st_d = _dev(lg), _dev(T), _dev(steps)
+    B, k = w.batch, w.top_k
+    tok = torch.full((B, 9), -7, dtype=torch.int32, device=hp.DEV)
+    idx = torch.full((B, 9, k), -7, dtype=torch.int32, device=hp.DEV)
+    prob = torch.full((B, 9, k), float("nan"), dtype=torch.float32, device=hp.DEV)
+    dec.dec_sample_topk_philox(lg_d, B, 9, w.vocab_valid, w.vocab_stride, T_d, k, seed, st_d,
+                               w.fill_token, tok, idx, prob)
+    u = orng.sample_uniforms(seed, steps, 9)
+    _compare(lg, w.vocab_valid, T, k, u, steps, w.fill_token, tok, idx, prob)
+    t2, i2, p2 = hp.sample(w, lg_d, T_d, _dev(u), step=st_d)
+    assert np.array_equal(hp.host(tok), hp.host(t2))
+    assert np.array_equal(hp.host(idx), hp.host(i2))
+    assert np.array_equal(_bits(prob), _bits(p2))
+
+
+def test_philox_sampler_without_step_uses_step_zero_and_no_delay():
+    w = configs.MINI_V1
+    lg, T = gen.logits(w), gen.temperatures(w)
+    seed = 424242
+    tok = torch.full((1, 9), -7, dtype=torch.int32, device=hp.DEV)
+    dec.dec_sample_topk_philox(_dev(lg), 1, 9, w.vocab_valid, w.vocab_stride, _dev(T), w.top_k,
+                               seed, None, w.fill_token, tok)
+    u = orng.sample_uniforms(seed, [0], 9)
+    t2, _, _ = hp.sample(w, _dev(lg), _dev(T), _dev(u))
+    assert np.array_equal(hp.host(tok), hp.host(t2))
+    assert np.all(hp.host(tok) != w.fill_token)
+
+
+def test_self_driving_captured_step_matches_oracle():
+    w = dataclasses.replace(configs.MINI_V1, n_layers=4, self_cap=512, self_len=200)
+    L0, N, seed = w.self_len, 4, 77
+    print(f"[selfdrive] NL={w.n_layers} L0={L0} replays={N}", flush=True)
+    d = wdev.step_inputs(w, hp.DEV)
+    kn, vn = gen.new_rows(w, "k", 0), gen.new_rows(w, "v", 0)
+    kn_d, vn_d = _dev(kn), _dev(vn)
+    len_g = torch.tensor([L0], dtype=torch.int32, device=hp.DEV)
+    step_g = torch.tensor([0], dtype=torch.int32, device=hp.DEV)
+    ws, nb = hp.workspace(w, w.self_cap, w.cross_cap)
+    o_s, o_c = hp.out_buf(w), hp.out_buf(w)
+    tok = torch.zeros((1, 9), dtype=torch.int32, device=hp.DEV)
+    idx = torch.zeros((1, 9, w.top_k), dtype=torch.int32, device=hp.DEV)
+    prob = torch.zeros((1, 9, w.top_k), dtype=torch.float32, device=hp.DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dec.dec_graph_begin(s)
+        dec.dec_kv_append(kn_d, vn_d, d["k_self"], d["v_self"], len_g, w.n_layers, 1, w.heads,
+                          w.self_cap, 64, dec.DEC_BF16, s)
+        dec.dec_attn_step(d["q_self"], d["k_self"], d["v_self"], len_g, w.self_cap, o_s,
+                          d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"], w.cross_cap,
+                          o_c, w.n_layers, 1, w.heads, 64, dec.DEC_BF16, w.scale, ws, nb, s)
+        dec.dec_sample_topk_philox(d["logits"], 1, 9, w.vocab_valid, w.vocab_stride,
+                                   d["temperature"], w.top_k, seed, step_g, w.fill_token, tok,
+                                   idx, prob, s)
+        dec.dec_step_advance(len_g, step_g, 1, s)
+        exe = dec.dec_graph_end(s)
+
+    # oracle state: generator rows below L0 - 1, then the appended row at every later slot
+    q = oattn.bf16_bits_to_f64(gen.queries(w, "self"))
+    K = [oattn.bf16_bits_to_f64(gen.kv_rows(w, "self", "k", l, 0, L0)) for l in range(w.n_layers)]
+    V = [oattn.bf16_bits_to_f64(gen.kv_rows(w, "self", "v", l, 0, L0)) for l in range(w.n_layers)]
+    lg, T = gen.logits(w), gen.temperatures(w)
+    try:
+        for i in range(N):
+            n = L0 + i
+            for l in range(w.n_layers):      # the row this replay appends
+                K[l] = np.concatenate([K[l][:, :n - 1], oattn.bf16_bits_to_f64(kn[l, 0])[:, None]], 1)
+                V[l] = np.concatenate([V[l][:, :n - 1], oattn.bf16_bits_to_f64(vn[l, 0])[:, None]], 1)
+            dec.dec_graph_launch(exe, s)
+            s.synchronize()
+            got = hp.host(o_s)
+            want = np.stack([np.stack([oattn.attend_one(q[l, 0, h], K[l][h], V[l][h], n, w.scale)
+                                       for h in range(w.heads)]) for l in range(w.n_layers)])
+            err = hp.row_rel_err(got[:, 0], want)
+            assert err <= BAR, f"replay {i}: self-attention rel err {err:.2e}"
+            u = orng.sample_uniforms(seed, [i], 9)
+            _compare(lg, w.vocab_valid, T, w.top_k, u, np.array([i], np.int32), w.fill_token,
+                     tok, idx, prob)
+            assert hp.host(len_g)[0] == n + 1 and hp.host(step_g)[0] == i + 1
+        kc = _bits(d["k_self"])[:, 0]
+        for l in range(w.n_layers):
+            for j in range(L0 - 1, L0 - 1 + N):
+                assert np.array_equal(kc[l, :, j], kn[l, 0]), (l, j)
+    finally:
+        dec.dec_graph_destroy(exe)

@@ -80,6 +80,7 @@ BY_NAME = {w.name: w for w in ALL}
 STREAM_Q_SELF, STREAM_K_SELF, STREAM_V_SELF = 0, 1, 2
 STREAM_Q_CROSS, STREAM_K_CROSS, STREAM_V_CROSS = 3, 4, 5
 STREAM_LENGTHS, STREAM_LOGITS, STREAM_UNIFORMS, STREAM_TEMPERATURE = 6, 7, 8, 9
+STREAM_K_NEW, STREAM_V_NEW = 10, 11           # the current token's key/value rows per step
 
 
 def valid_kv_bytes(w: Workload, self_lens, cross_lens) -> int:

@@ -27,7 +27,7 @@ import numpy as np
 from .configs import (SEED_ROOT, STREAM_Q_SELF, STREAM_K_SELF, STREAM_V_SELF,
                       STREAM_Q_CROSS, STREAM_K_CROSS, STREAM_V_CROSS,
                       STREAM_LENGTHS, STREAM_LOGITS, STREAM_UNIFORMS,
-                      STREAM_TEMPERATURE, Workload)
+                      STREAM_TEMPERATURE, STREAM_K_NEW, STREAM_V_NEW, Workload)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -128,6 +128,14 @@ def cache(w: Workload, kind: str, which: str, lens, invalid="nan", threads=None,
     with ThreadPoolExecutor(nthreads) as ex:
         list(ex.map(one, jobs))
     return out
+
+
+def new_rows(w: Workload, which: str, step: int = 0):
+    """The current token's self-attention key ("k") or value ("v") row for every
+    (layer, sequence, head) at a step: [n_layers, B, H, hd]."""
+    stream = STREAM_K_NEW if which == "k" else STREAM_V_NEW
+    return _normals(rng_for(w.cfg_id, stream, 0, 0, step),
+                    (w.n_layers, w.batch, w.heads, w.head_dim), w.qkv_std, w.dtype)
 
 
 def logits(w: Workload, step: int = 0, pad_value=1e30):
