@@ -23,7 +23,8 @@ Source: the "Optimized Parler TTS" page.
     c lagging c steps ("A rough architecture of Parler TTS", the delay-pattern
     figure taken from the MusicGen paper).
   * cache.py      -- writing the current token's key/value row into the
-    preallocated cache ("Analysis and improvements": static caches).
+    preallocated cache ("Analysis and improvements": static caches), and the
+    key order of a paged cache ("Future work": paged attention).
   * rng.py        -- counter-based uniforms (Philox4x64-10 from its published
     definition), so sampling needs no random numbers from the host
     ("Analysis and improvements": sampling without a GPU/CPU synchronisation).

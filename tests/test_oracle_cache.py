@@ -29,3 +29,36 @@ def test_append_out_of_range_lengths_write_nothing():
     kn = np.ones((1, 2, 1, 2), np.float32)
     gk, gv = cache.append(kn, kn, k.copy(), v.copy(), [-1, 4])
     assert not gk.any() and not gv.any()
+
+
+def test_gather_paged_hand_built():
+    # 2 layers, 3 physical blocks of 2 rows, 1 head, hd 1; values name (layer, block, row)
+    pool = np.zeros((2, 3, 1, 2, 1), np.float32)
+    for layer in range(2):
+        for blk in range(3):
+            for r in range(2):
+                pool[layer, blk, 0, r, 0] = 100 * layer + 10 * blk + r
+    table = np.array([[2, 0, 1], [1, 1, 1]], np.int32)
+    got = cache.gather_paged(pool, table, 2, 1, 0, 0, 5)[:, 0]
+    assert got.tolist() == [120, 121, 100, 101, 110]     # blocks 2, 0, 1 of layer 1
+    got = cache.gather_paged(pool, table, 2, 0, 1, 0, 3)[:, 0]
+    assert got.tolist() == [10, 11, 10]                  # a table may repeat a block
+    assert cache.gather_paged(pool, table, 2, 0, 0, 0, 0).shape == (0, 1)
+
+
+def test_gather_paged_identity_table_is_the_static_layout():
+    # with table[b, i] = b * nb + i the pool holds exactly the static cache's rows
+    rng = np.random.default_rng(3)
+    NL, B, H, bs, nb, hd = 2, 3, 2, 4, 5, 3
+    static = rng.standard_normal((NL, B, H, nb * bs, hd)).astype(np.float32)
+    pool = np.zeros((NL, B * nb, H, bs, hd), np.float32)
+    for b in range(B):
+        for i in range(nb):
+            pool[:, b * nb + i] = static[:, b, :, i * bs:(i + 1) * bs]
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)
+    for layer in range(NL):
+        for b in range(B):
+            for h in range(H):
+                for n in (0, 1, 4, 5, 17, 20):
+                    assert np.array_equal(cache.gather_paged(pool, table, bs, layer, b, h, n),
+                                          static[layer, b, h, :n])
