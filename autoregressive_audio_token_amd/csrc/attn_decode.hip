@@ -238,7 +238,15 @@ struct Tile {
   }
 };
 
-template <typename T>
+// Buffer descriptors for one tile's K and V rows, and the tile's first row inside them.
+struct TileAddr {
+  __amdgpu_buffer_rsrc_t k, v;
+  int row0;
+};
+
+// PAGED: segments with a block table read each tile through a descriptor over its block of
+// the pool (a 64-key tile never crosses a block); other segments read the static layout.
+template <typename T, bool PAGED>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p) {
   constexpr int HD = kAttnHeadDim;
   using TileT = Tile<T>;
@@ -399,38 +407,71 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       continue;
     }
 
-    const T* qp = static_cast<const T*>(S.q) + wave_sidx * HD;
-    const T* kp = static_cast<const T*>(S.k) + wave_sidx * (size_t)S.L_cap * HD;
-    const T* vp = static_cast<const T*>(S.v) + wave_sidx * (size_t)S.L_cap * HD;
+    constexpr int kStep = kAttnWaves * kAttnKeysPerTile;  // keys between a wave's tiles
+    constexpr int kRowBytes = HD * (int)sizeof(T);
+    const int lane_off = kg * kRowBytes + dl * 16;
+    const bool paged = PAGED && S.table != nullptr;  // uniform: per segment
+    const T* kp = static_cast<const T*>(S.k);
+    const T* vp = static_cast<const T*>(S.v);
+    size_t head_off = 0;  // paged: offset of (layer, head) inside a block, before the block term
+    if (paged) {
+      head_off = (size_t)(wlh / p.H) * S.n_blocks;  // layer's first block
+    } else {
+      kp += wave_sidx * (size_t)S.L_cap * HD;
+      vp += wave_sidx * (size_t)S.L_cap * HD;
+    }
+    // static: one descriptor over the whole valid prefix
+    const __amdgpu_buffer_rsrc_t rk_seq = rows_rsrc(kp, paged ? 0 : n, kRowBytes);
+    const __amdgpu_buffer_rsrc_t rv_seq = rows_rsrc(vp, paged ? 0 : n, kRowBytes);
+    const __amdgpu_buffer_rsrc_t rk_none = rows_rsrc(kp, 0, kRowBytes);  // no rows: no traffic
+    const __amdgpu_buffer_rsrc_t rv_none = rows_rsrc(vp, 0, kRowBytes);
     float fm = 0.f, fl = 0.f, fa = 0.f;  // running fold (combining threads)
+    const T* qp = static_cast<const T*>(S.q) + wave_sidx * HD + dl * EPL;
 
     for (int c = c0; c < c1; ++c) {
-      // tile t of this wave starts at key tile_base(t); packed items read one tile
+      // tile t of this wave starts at key cb + t * kStep; packed items read one tile
       const int cb = c * kAttnChunk + wave_part * kAttnKeysPerTile;
       float m_g = -INFINITY, l_g = 0.f;  // this lane group's online state
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
       if (wave_ok && cb < n) {  // uniform across the wave
-        constexpr int kStep = kAttnWaves * kAttnKeysPerTile;  // keys between a wave's tiles
-        constexpr int kRowBytes = HD * (int)sizeof(T);
         const int nt = packed ? 1 : min(TPC, (n - cb + kStep - 1) / kStep);
-        const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kp, n, kRowBytes);
-        const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vp, n, kRowBytes);
-        const int lane_off = kg * kRowBytes + dl * 16;
+        // paged: lane i < nt holds the physical block of the wave's tile i in this chunk
+        int blk_of = 0;
+        if (paged && lane < nt)
+          blk_of = S.table[(size_t)b * S.table_stride + ((cb + lane * kStep) >> S.bs_log2)];
+        auto addr = [&](int t) -> TileAddr {
+          const int base = cb + t * kStep;
+          // past this wave's tiles of the chunk: a descriptor with no rows, so the
+          // pipeline's last prefetch moves no bytes (the next chunk loads its own)
+          if (t >= nt) return {rk_none, rv_none, 0};
+          if (!paged) return {rk_seq, rv_seq, base};
+          const int bs = 1 << S.bs_log2;
+          const int row = base & (bs - 1);
+          const int blk = __builtin_amdgcn_readlane(blk_of, t);
+          // rows of this tile inside its block; none past n or for an entry outside the pool
+          int rows = base < n ? min(bs - row, n - base) : 0;
+          if (blk < 0 || blk >= S.n_blocks) rows = 0;
+          const size_t off = (((head_off + (size_t)(unsigned)blk) * p.H + (wlh % p.H)) * bs + row) * HD;
+          return {rows_rsrc(kp + off, rows, kRowBytes), rows_rsrc(vp + off, rows, kRowBytes), 0};
+        };
         TileT ta, tb;
-        ta.load(rk, rv, cb, lane_off);
-        QSlice<T> qs;
-        qs.load(qp + dl * EPL, p.qscale);
-        // ping-pong: the next tile is in flight while one is consumed (past the
-        // last tile the prefetch lies wholly outside the descriptor: no traffic)
+        const TileAddr a0 = addr(0);
+        ta.load(a0.k, a0.v, a0.row0, lane_off);
+        QSlice<T> qs;  // after the first tile's loads, so K/V requests leave first
+        qs.load(qp, p.qscale);
+        // ping-pong: the next tile is in flight while one is consumed (past n the
+        // prefetch lies wholly outside its descriptor: no traffic)
 #pragma nounroll
         for (int t = 0; t < nt; t += 2) {
           const int base = cb + t * kStep;
-          tb.load(rk, rv, base + kStep, lane_off);
+          const TileAddr a1 = addr(t + 1);
+          tb.load(a1.k, a1.v, a1.row0, lane_off);
           ta.consume(qs, base, n, kg, m_g, l_g, acc);
           if (t + 1 >= nt) break;
-          ta.load(rk, rv, base + 2 * kStep, lane_off);
+          const TileAddr a2 = addr(t + 2);
+          ta.load(a2.k, a2.v, a2.row0, lane_off);
           tb.consume(qs, base + kStep, n, kg, m_g, l_g, acc);
         }
       }
@@ -519,20 +560,22 @@ long long attn_items_cap(const AttnParams& p) {
 namespace {
 struct DevInfo {
   int cus = 0;
-  int occ[2] = {0, 0};  // resident workgroups per CU, per dtype, at the small-LDS size
+  int occ[2][2] = {{0, 0}, {0, 0}};  // resident workgroups per CU [dtype][paged], small LDS
 };
 DevInfo g_dev[64];
 }  // namespace
 
-template <typename T>
+template <typename T, bool PAGED>
 static void* attn_kernel_ptr() {
-  return reinterpret_cast<void*>(&attn_decode_kernel<T>);
+  return reinterpret_cast<void*>(&attn_decode_kernel<T, PAGED>);
 }
 
 hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream) {
   const int G = p.nseg * p.B;
   const size_t lds = (size_t)(3 * G + 1) * sizeof(int);
-  void* fn = dtype == 0 ? attn_kernel_ptr<uint16_t>() : attn_kernel_ptr<float>();
+  const bool paged = p.seg[0].table != nullptr || (p.nseg > 1 && p.seg[1].table != nullptr);
+  void* fn = dtype == 0 ? (paged ? attn_kernel_ptr<uint16_t, true>() : attn_kernel_ptr<uint16_t, false>())
+                        : (paged ? attn_kernel_ptr<float, true>() : attn_kernel_ptr<float, false>());
   if (blocks <= 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -544,22 +587,26 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
       if (e != hipSuccess) return e;
       di.cus = cus;
     }
-    int occ = di.occ[dtype];
+    int occ = di.occ[dtype][paged ? 1 : 0];
     if (occ == 0 || G > 64) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);
       if (e != hipSuccess) return e;
       if (occ < 1) occ = 1;
-      if (G <= 64) di.occ[dtype] = occ;
+      if (G <= 64) di.occ[dtype][paged ? 1 : 0] = occ;
     }
     const long long cap = attn_items_cap(p);
     const long long want = (long long)di.cus * occ;
     blocks = (int)(want < cap ? want : cap);
   }
   if (blocks < 1) blocks = 1;
-  if (dtype == 0) {
-    hipLaunchKernelGGL(attn_decode_kernel<uint16_t>, dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+  if (dtype == 0 && !paged) {
+    hipLaunchKernelGGL((attn_decode_kernel<uint16_t, false>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+  } else if (dtype == 0) {
+    hipLaunchKernelGGL((attn_decode_kernel<uint16_t, true>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+  } else if (!paged) {
+    hipLaunchKernelGGL((attn_decode_kernel<float, false>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+    hipLaunchKernelGGL((attn_decode_kernel<float, true>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
   }
   return hipGetLastError();
 }

@@ -41,8 +41,13 @@ struct AttnSeg {
   float* out;             // [NL, B, H, 64]
   float* part;            // [NL*B*H, nck_cap, kAttnPartStride] chunk partials (split mode)
   int32_t* ticket;        // [NL*B*H] chunk arrival counters (split mode), zero between calls
-  int L_cap;
+  int L_cap;              // keys a sequence can hold (paged: table_stride << bs_log2)
   int nck_cap;            // ceil(L_cap / kAttnChunk)
+  // paged cache (table != nullptr): k, v are pools [NL, n_blocks, H, 1 << bs_log2, 64]
+  const int32_t* table;   // [B, table_stride] physical block of each logical block
+  int table_stride;
+  int n_blocks;           // physical blocks per layer
+  int bs_log2;            // log2(keys per block), at least log2(64)
 };
 
 struct AttnParams {

@@ -62,7 +62,14 @@ struct SegArgs {
   const int32_t* len;
   float* out;
   int L_cap;
+  // paged cache: k, v are block pools; L_cap = table_stride * block_size
+  const int32_t* table = nullptr;
+  int table_stride = 0;
+  int n_blocks = 0;
+  int block_size = 0;
 };
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int dtype,
                 float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -72,6 +79,18 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   if (dtype != DEC_BF16 && dtype != DEC_F32) return DEC_E_DTYPE;
   for (int s = 0; s < nseg; ++s) {
     if (!sizes_ok(NL, B, H, segs[s].L_cap)) return DEC_E_SHAPE;
+  }
+  for (int s = 0; s < nseg; ++s) {
+    const SegArgs& a = segs[s];
+    if (a.table == nullptr) continue;
+    const long long row = (long long)hd * (dtype == DEC_BF16 ? 2 : 4);
+    if (a.n_blocks < 1 || a.table_stride < 1) return DEC_E_SHAPE;
+    if ((long long)NL * a.n_blocks * H * a.block_size * row > (1LL << 46)) return DEC_E_SHAPE;
+    if ((long long)B * a.table_stride > (1LL << 30)) return DEC_E_SHAPE;
+    if (!is_pow2(a.block_size) || a.block_size < dec::kAttnKeysPerTile ||
+        a.block_size > (1 << 20))
+      return DEC_E_UNSUPPORTED;
+    if (!aligned(a.table, 4)) return DEC_E_ALIGN;
   }
   if (hd != dec::kAttnHeadDim) return DEC_E_UNSUPPORTED;
   if (nseg * B > dec::kAttnMaxGroups) return DEC_E_UNSUPPORTED;
@@ -109,6 +128,10 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.out = segs[s].out;
     g.L_cap = segs[s].L_cap;
     g.nck_cap = lay[s].nck_cap;
+    g.table = segs[s].table;
+    g.table_stride = segs[s].table_stride;
+    g.n_blocks = segs[s].n_blocks;
+    g.bs_log2 = segs[s].table ? __builtin_ctz((unsigned)segs[s].block_size) : 0;
     if (lay[s].bytes > 0) {
       char* base = static_cast<char*>(ws) + off;
       g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
@@ -173,6 +196,43 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self, co
                   size_t ws_bytes, dec_stream_t stream) {
   const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
                         {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_self_paged(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* len, float* out,
+                        int n_layers, int B, int H, int hd, int block_size, int n_blocks,
+                        int max_blocks, int dtype, float scale, void* workspace,
+                        size_t ws_bytes, dec_stream_t stream) {
+  if (!block_table) return DEC_E_NULL;
+  if (max_blocks < 1 || block_size < 1 || (long long)max_blocks * block_size > (1LL << 30))
+    return DEC_E_SHAPE;
+  SegArgs a{q, k_pool, v_pool, len, out, max_blocks * block_size};
+  a.table = block_table;
+  a.table_stride = max_blocks;
+  a.n_blocks = n_blocks;
+  a.block_size = block_size;
+  return attn_common(&a, 1, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_step_paged(const void* q_self, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* len, int block_size,
+                        int n_blocks, int max_blocks, float* out_self, const void* q_cross,
+                        const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                        int L_cap_cross, float* out_cross, int n_layers, int B, int H, int hd,
+                        int dtype, float scale, void* workspace, size_t ws_bytes,
+                        dec_stream_t stream) {
+  if (!block_table) return DEC_E_NULL;
+  if (max_blocks < 1 || block_size < 1 || (long long)max_blocks * block_size > (1LL << 30))
+    return DEC_E_SHAPE;
+  SegArgs s[2] = {{q_self, k_pool, v_pool, len, out_self, max_blocks * block_size},
+                  {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  s[0].table = block_table;
+  s[0].table_stride = max_blocks;
+  s[0].n_blocks = n_blocks;
+  s[0].block_size = block_size;
   return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
                      reinterpret_cast<hipStream_t>(stream));
 }

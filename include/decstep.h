@@ -116,6 +116,41 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
                   int n_layers, int B, int H, int hd, int dtype, float scale,
                   void* workspace, size_t ws_bytes, dec_stream_t stream);
 
+/* Self-attention over a PAGED cache ("Future work": paged attention, so a
+ * sequence's keys live in fixed-size blocks drawn from a shared pool instead of
+ * one preallocated run of L_cap slots).  Same arithmetic as dec_attn_self; only
+ * the address of each key changes, so for equal logical contents the outputs are
+ * bit-identical to dec_attn_self.
+ *
+ *   q            [n_layers, B, H, hd]                         dtype
+ *   k_pool,
+ *   v_pool       [n_layers, n_blocks, H, block_size, hd]      dtype
+ *   block_table  [B, max_blocks] int32: key j of sequence b is row j % block_size
+ *                of physical block block_table[b][j / block_size] (the same
+ *                table for every layer and head)
+ *   len          [B] int32, clamped to [0, max_blocks * block_size]
+ *   out          [n_layers, B, H, hd] float32
+ * block_size: a power of two, at least 64 (a 64-key tile never crosses a block),
+ * else DEC_E_UNSUPPORTED.  Workspace: dec_attn_workspace_bytes with
+ * L_cap_self = max_blocks * block_size.  Device-side: a table entry outside
+ * [0, n_blocks) makes that block read as zero rows (nothing outside the pool is
+ * touched); entries past ceil(len[b] / block_size) are never read. */
+int dec_attn_self_paged(const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* len, float* out,
+                        int n_layers, int B, int H, int hd, int block_size, int n_blocks,
+                        int max_blocks, int dtype, float scale, void* workspace,
+                        size_t ws_bytes, dec_stream_t stream);
+
+/* dec_attn_step with the self-attention cache paged (as dec_attn_self_paged) and
+ * the description cache static, in one launch. */
+int dec_attn_step_paged(const void* q_self, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* len, int block_size,
+                        int n_blocks, int max_blocks, float* out_self, const void* q_cross,
+                        const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                        int L_cap_cross, float* out_cross, int n_layers, int B, int H, int hd,
+                        int dtype, float scale, void* workspace, size_t ws_bytes,
+                        dec_stream_t stream);
+
 /* Fused temperature / top-k / softmax / sampling of the next token of every
  * codebook, with the codebook delay mask ("Future work", item 2: one kernel in
  * place of the temperature, top-k and softmax kernels; "Analysis and

@@ -131,6 +131,39 @@ def test_sampler_host_validation():
     assert _samp(idx=A + 1) == D.DEC_E_ALIGN
 
 
+def _paged(**kw):
+    a = dict(q=A, k=A, v=A, tab=A, len=A, out=A, NL=24, B=1, H=16, hd=64, bs=64, nb=100, mb=64,
+             dt=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return D.raw_status("dec_attn_self_paged", a["q"], a["k"], a["v"], a["tab"], a["len"],
+                        a["out"], a["NL"], a["B"], a["H"], a["hd"], a["bs"], a["nb"], a["mb"],
+                        a["dt"], ctypes.c_float(0.125), a["ws"], a["wsb"], None)
+
+
+@_no_gpu
+def test_paged_attention_host_validation():
+    for k in ("q", "k", "v", "tab", "len", "out"):
+        assert _paged(**{k: None}) == D.DEC_E_NULL, k
+    assert _paged(dt=5) == D.DEC_E_DTYPE
+    for bad in (dict(nb=0), dict(mb=0), dict(bs=0), dict(NL=0), dict(B=0),
+                dict(mb=1 << 20, bs=1 << 12), dict(nb=1 << 30)):
+        assert _paged(**bad) == D.DEC_E_SHAPE, bad
+    for bad in (dict(bs=32), dict(bs=96), dict(bs=1 << 21), dict(hd=128)):
+        assert _paged(**bad) == D.DEC_E_UNSUPPORTED, bad
+    assert _paged(tab=A + 2) == D.DEC_E_ALIGN
+    assert _paged(k=A + 8) == D.DEC_E_ALIGN
+    need = dec.dec_attn_workspace_bytes(24, 1, 16, 64, 64 * 64, 0)
+    assert need > 0
+    assert _paged(wsb=need - 1) == D.DEC_E_WORKSPACE
+    assert _paged(ws=None) == D.DEC_E_NULL
+    st = D.raw_status("dec_attn_step_paged", A, A, A, None, A, 64, 100, 64, A, A, A, A, A, 64, A,
+                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, 1 << 30, None)
+    assert st == D.DEC_E_NULL
+    st = D.raw_status("dec_attn_step_paged", A, A, A, A, A, 48, 100, 64, A, A, A, A, A, 64, A,
+                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, 1 << 30, None)
+    assert st == D.DEC_E_UNSUPPORTED
+
+
 def _samp_rng(**kw):
     a = dict(lg=A, B=1, ncb=9, V=1089, S=1096, T=A, k=50, seed=7, step=None, fill=1089, tok=A,
              idx=None, prob=None)
