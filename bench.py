@@ -35,6 +35,9 @@ def parse(argv=None):
                     help="event-timed attention launches for the roofline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged", type=int, default=0, metavar="BS",
+                    help="self-attention cache as a paged block pool with BS keys per block\n"
+                         "(blocks scattered by a seeded permutation); 0: the static cache")
     ap.add_argument("--eager", action="store_true",
                     help="run warmup + steps eager steps (no graph, no timing) and exit;\n"
                          "the launch sequence the hardware-counter runs profile")
@@ -188,7 +191,36 @@ def main(argv=None):
     step_t = d["step"] if w.delay else None
     stream = torch.cuda.Stream(device=dev)
 
+    if a.paged:
+        # every cache set's self cache scattered over a pool: logical block i of sequence b
+        # lives in physical block table[b, i]; the pool holds one spare block per sequence
+        bs = a.paged
+        mb = w.self_cap // bs
+        n_blocks = w.batch * (mb + 1)
+        perm = np.random.default_rng(12345).permutation(n_blocks)[:w.batch * mb]
+        table_h = perm.reshape(w.batch, mb).astype(np.int32)
+        table = torch.from_numpy(table_h).to(dev)
+        idx = torch.from_numpy(table_h.reshape(-1)).to(dev).long()
+        for st in sets:
+            for which in ("k_self", "v_self"):
+                src = st[which]                       # [NL, B, H, L_cap, hd]
+                pool = torch.full((w.n_layers, n_blocks, w.heads, bs, w.head_dim), float("nan"),
+                                  dtype=src.dtype, device=dev)
+                blocks = src.view(w.n_layers, w.batch, w.heads, mb, bs, w.head_dim)
+                blocks = blocks.permute(0, 1, 3, 2, 4, 5).reshape(
+                    w.n_layers, w.batch * mb, w.heads, bs, w.head_dim)
+                pool[:, idx] = blocks
+                st[which] = pool
+        torch.cuda.synchronize()
+
     def attn(st, s):
+        if a.paged:
+            dec.dec_attn_step_paged(d["q_self"], st["k_self"], st["v_self"], table, d["len"],
+                                    a.paged, n_blocks, w.self_cap // a.paged, o_s, d["q_cross"],
+                                    st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap, o_c,
+                                    w.n_layers, w.batch, w.heads, w.head_dim, code, w.scale, ws,
+                                    nb, s)
+            return
         dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], d["len"], w.self_cap, o_s,
                           d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
                           o_c, w.n_layers, w.batch, w.heads, w.head_dim, code, w.scale, ws, nb,
@@ -281,6 +313,8 @@ def main(argv=None):
     achieved = valid / (k_us * 1e-6) / 1e9
     dec.dec_graph_destroy(graph)
     traffic_rec, traffic_why = counter_traffic(w.name)
+    if a.paged:
+        traffic_rec, traffic_why = None, "counters describe the static layout"
 
     result = {
         "metric": METRIC,
@@ -304,11 +338,16 @@ def main(argv=None):
             "vocab_stride": w.vocab_stride, "top_k": w.top_k, "accumulate": "f32",
             "valid_kv_bytes_per_step": valid, "cache_sets": R,
             "static_cache_bytes_per_set": static_bytes,
-            "schedule": "hipGraph of R steps; step = dec_attn_step (self+cross, all layers, "
-                        "one launch) + dec_sample_topk",
+            "kv_layout": (f"self cache paged, {a.paged} keys per block" if a.paged
+                          else "static caches"),
+            "schedule": f"hipGraph of R steps; step = "
+                        f"{'dec_attn_step_paged' if a.paged else 'dec_attn_step'} (self+cross, "
+                        f"all layers, one launch) + dec_sample_topk",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "attn_decode_kernel (dec_attn_step)",
+            "bound": "hbm",
+            "kernel": ("attn_decode_kernel (dec_attn_step_paged)" if a.paged
+                       else "attn_decode_kernel (dec_attn_step)"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None,
