@@ -25,6 +25,8 @@ Source: the "Optimized Parler TTS" page.
   * cache.py      -- writing the current token's key/value row into the
     preallocated cache ("Analysis and improvements": static caches), and the
     key order of a paged cache ("Future work": paged attention).
+  * heads.py      -- the merged 9-codebook LM head on the last position and the
+    merged 9-codebook embedding lookup ("Analysis and improvements").
   * rng.py        -- counter-based uniforms (Philox4x64-10 from its published
     definition), so sampling needs no random numbers from the host
     ("Analysis and improvements": sampling without a GPU/CPU synchronisation).
@@ -33,4 +35,4 @@ Every function here is pinned by a CPU test against something other than
 itself (closed forms, library routines, brute force, invariants); none is
 "parity unpinned".
 """
-from . import attn, sampling, delay, cache, rng  # noqa: F401
+from . import attn, sampling, delay, cache, rng, heads  # noqa: F401
