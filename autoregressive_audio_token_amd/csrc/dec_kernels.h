@@ -83,6 +83,28 @@ struct SampleParams {
 
 hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
 
+// ---- merged LM head and embedding sum ----------------------------------------------------
+
+constexpr int kHeadWaves = 4;   // 8-row groups (one per wave) per workgroup
+constexpr int kHeadBT = 16;     // rows of h staged in LDS at a time
+
+struct HeadParams {
+  const uint16_t* h;      // [B, D] bf16
+  const uint16_t* W;      // [n_cb, V_stride, D] bf16
+  float* logits;          // [B, n_cb, V_stride]; columns >= V_valid untouched
+  int B, D, n_cb, V_valid, V_stride;
+};
+
+struct EmbedParams {
+  const int32_t* tokens;  // [B, n_cb]
+  const uint16_t* E;      // [n_cb, V_emb, D] bf16
+  float* x;               // [B, D]
+  int B, n_cb, V_emb, D;
+};
+
+hipError_t lm_head_launch(const HeadParams& p, hipStream_t stream);
+hipError_t embed_sum_launch(const EmbedParams& p, hipStream_t stream);
+
 // ---- small utility kernels ------------------------------------------------------------
 
 hipError_t fill_zero_launch(void* ptr, size_t bytes, hipStream_t stream);

@@ -328,6 +328,47 @@ int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
+int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n_cb,
+                int V_valid, int V_stride, dec_stream_t stream) {
+  if (!h || !W || !logits) return DEC_E_NULL;
+  if (B < 1 || n_cb < 1 || V_valid < 1 || V_stride < V_valid || D < 1) return DEC_E_SHAPE;
+  if ((long long)B * n_cb * V_stride > (1LL << 40) || (long long)n_cb * V_stride > (1 << 24))
+    return DEC_E_SHAPE;
+  if (D != 512 && D != 768 && D != 1024 && D != 1536 && D != 2048) return DEC_E_UNSUPPORTED;
+  if ((long long)V_valid * D * 2 > (1LL << 31) - 1) return DEC_E_UNSUPPORTED;
+  if (!aligned(h, 16) || !aligned(W, 16) || !aligned(logits, 4)) return DEC_E_ALIGN;
+  dec::HeadParams p{};
+  p.h = static_cast<const uint16_t*>(h);
+  p.W = static_cast<const uint16_t*>(W);
+  p.logits = logits;
+  p.B = B;
+  p.D = D;
+  p.n_cb = n_cb;
+  p.V_valid = V_valid;
+  p.V_stride = V_stride;
+  const hipError_t e = dec::lm_head_launch(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_embed_sum(const int32_t* tokens, const void* E, float* x, int B, int n_cb, int V_emb,
+                  int D, dec_stream_t stream) {
+  if (!tokens || !E || !x) return DEC_E_NULL;
+  if (B < 1 || B > 65535 || n_cb < 1 || V_emb < 1 || D < 1) return DEC_E_SHAPE;
+  if ((long long)n_cb * V_emb * D > (1LL << 40)) return DEC_E_SHAPE;
+  if (D % 8 != 0) return DEC_E_UNSUPPORTED;
+  if (!aligned(tokens, 4) || !aligned(E, 16) || !aligned(x, 16)) return DEC_E_ALIGN;
+  dec::EmbedParams p{};
+  p.tokens = tokens;
+  p.E = static_cast<const uint16_t*>(E);
+  p.x = x;
+  p.B = B;
+  p.n_cb = n_cb;
+  p.V_emb = V_emb;
+  p.D = D;
+  const hipError_t e = dec::embed_sum_launch(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream) {
   if (B < 1) return DEC_E_SHAPE;
   if (len == nullptr && step == nullptr) return DEC_E_NULL;

@@ -1,0 +1,138 @@
+// The merged 9-codebook LM head on the last position and the merged 9-codebook
+// embedding sum (gfx950).
+//
+// "Optimized Parler TTS", "Analysis and improvements": logits are produced for
+// the last position only, the nine LM heads are merged into one weight matrix,
+// and the nine embedding lookups into one gather.  "A rough architecture of
+// Parler TTS": the decoder takes the nine tokens of a step at once, so its
+// input is the sum of the nine codebooks' embedding rows.
+//
+// LM head: logits[b, c, v] = <h[b], W[c, v]> for v < V_valid.  At decode batch
+// sizes this is a matrix-vector product bound by reading W once (~20 MB at
+// 9 x 1089 x 1024 bf16), so it runs on the vector ALU with v_dot2c_f32_bf16, not
+// MFMA.  A wave owns 8 consecutive rows of one codebook, one row per group of 8
+// lanes; a lane reads 16 bytes of each 128-byte segment of its row, so every
+// load instruction covers whole cache lines, and all of the wave's loads are in
+// flight before h is needed.  A buffer descriptor spans the codebook's V_valid
+// rows, so the padding rows of a partial last group are never read.  h is
+// staged in LDS in batch tiles of kHeadBT rows and read back per segment; the
+// 8 lanes of a row reduce with DPP.
+#include "dec_common.h"
+#include "dec_kernels.h"
+
+namespace dec {
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float s) {
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.z), as_bf16x2(b.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.w), as_bf16x2(b.w), s, false);
+  return s;
+}
+
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNonTemporal = 2;
+
+}  // namespace
+
+template <int NSEG>
+__global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_kernel(HeadParams p) {
+  constexpr int D = NSEG * 64;
+  __shared__ u32x4 s_h[kHeadBT * D / 8];  // kHeadBT rows of h, bf16
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int grp = lane >> 3;  // row within the wave's 8
+  const int sl = lane & 7;    // 16-byte slice of each 128-byte segment
+  const int rgpc = (p.V_valid + 7) >> 3;  // 8-row groups per codebook
+  const int rg = blockIdx.x * kHeadWaves + wave;
+  const bool active = rg < p.n_cb * rgpc;  // uniform per wave
+  const int c = active ? rg / rgpc : 0;
+  const int v = (active ? rg - c * rgpc : 0) * 8 + grp;
+
+  // W rows of codebook c: rows at or past V_valid lie outside the descriptor
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.W + (size_t)c * p.V_stride * D), 0,
+      active ? p.V_valid * D * 2 : 0, kBufWord3);
+  u32x4 w[NSEG];
+  const int row_off = v * D * 2 + sl * 16;
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+    w[s] = __builtin_amdgcn_raw_buffer_load_b128(rw, row_off + s * 128, 0, kBufNonTemporal);
+
+  for (int b0 = 0; b0 < p.B; b0 += kHeadBT) {
+    const int bt = min(kHeadBT, p.B - b0);
+    __syncthreads();  // the previous tile of h has been read
+    const u32x4* hs = reinterpret_cast<const u32x4*>(p.h + (size_t)b0 * D);
+    for (int i = tid; i < bt * D / 8; i += kHeadWaves * kWave) s_h[i] = hs[i];
+    __syncthreads();
+    if (!active) continue;
+    for (int bb = 0; bb < bt; ++bb) {
+      float acc = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) acc = dot8(w[s], s_h[bb * (D / 8) + s * 8 + sl], acc);
+      acc = group_sum<8>(acc);
+      if (sl == 0 && v < p.V_valid)
+        p.logits[((size_t)(b0 + bb) * p.n_cb + c) * p.V_stride + v] = acc;
+    }
+  }
+}
+
+template <int NSEG>
+static hipError_t lm_head_launch_n(const HeadParams& p, hipStream_t stream) {
+  const int groups = p.n_cb * ((p.V_valid + 7) / 8);
+  const int blocks = (groups + kHeadWaves - 1) / kHeadWaves;
+  hipLaunchKernelGGL(lm_head_kernel<NSEG>, dim3(blocks), dim3(kHeadWaves * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t lm_head_launch(const HeadParams& p, hipStream_t stream) {
+  switch (p.D) {
+    case 512: return lm_head_launch_n<8>(p, stream);
+    case 768: return lm_head_launch_n<12>(p, stream);
+    case 1024: return lm_head_launch_n<16>(p, stream);
+    case 1536: return lm_head_launch_n<24>(p, stream);
+    case 2048: return lm_head_launch_n<32>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// x[b, :] = sum_c E[c, tokens[b, c], :]; tokens outside [0, V_emb) add nothing.
+// One workgroup per (sequence, 16-byte column slice block); fp32 accumulation in
+// codebook order.
+__global__ __launch_bounds__(256) void embed_sum_kernel(EmbedParams p) {
+  const int b = blockIdx.y;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 8;  // bf16 element
+  if (col >= p.D) return;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int c = 0; c < p.n_cb; ++c) {
+    const int t = p.tokens[(size_t)b * p.n_cb + c];
+    if (t < 0 || t >= p.V_emb) continue;  // uniform across the workgroup
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p.E + ((size_t)c * p.V_emb + t) * p.D + col);
+    acc[0] += bf16_lo(r.x); acc[1] += bf16_hi(r.x);
+    acc[2] += bf16_lo(r.y); acc[3] += bf16_hi(r.y);
+    acc[4] += bf16_lo(r.z); acc[5] += bf16_hi(r.z);
+    acc[6] += bf16_lo(r.w); acc[7] += bf16_hi(r.w);
+  }
+  float4* out = reinterpret_cast<float4*>(p.x + (size_t)b * p.D + col);
+  out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+hipError_t embed_sum_launch(const EmbedParams& p, hipStream_t stream) {
+  const int threads = 128;
+  const int per_b = (p.D / 8 + threads - 1) / threads;
+  hipLaunchKernelGGL(embed_sum_kernel, dim3(per_b, p.B), dim3(threads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace dec

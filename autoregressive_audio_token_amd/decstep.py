@@ -62,6 +62,8 @@ _SIGS = {
     "dec_sample_topk_philox": (_I, [_P, _I, _I, _I, _I, _P, _I, ctypes.c_uint64, _P,
                                     ctypes.c_int32, _P, _P, _P, _P]),
     "dec_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "dec_lm_head": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "dec_embed_sum": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "dec_step_advance": (_I, [_P, _P, _I, _P]),
     "dec_graph_begin": (_I, [_P]),
     "dec_graph_end": (_I, [_P, ctypes.POINTER(_P)]),
@@ -194,6 +196,16 @@ def dec_kv_append(k_new, v_new, k_cache, v_cache, len, n_layers, B, H, L_cap, hd
                   stream=None):
     _check(_lib.dec_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(len),
                               n_layers, B, H, L_cap, hd, dtype, _stream(stream)))
+
+
+def dec_lm_head(h, W, logits, B, D, n_cb, V_valid, V_stride, stream=None):
+    _check(_lib.dec_lm_head(_ptr(h), _ptr(W), _ptr(logits), B, D, n_cb, V_valid, V_stride,
+                            _stream(stream)))
+
+
+def dec_embed_sum(tokens, E, x, B, n_cb, V_emb, D, stream=None):
+    _check(_lib.dec_embed_sum(_ptr(tokens), _ptr(E), _ptr(x), B, n_cb, V_emb, D,
+                              _stream(stream)))
 
 
 def dec_step_advance(len, step, B, stream=None):

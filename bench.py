@@ -38,6 +38,9 @@ def parse(argv=None):
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="self-attention cache as a paged block pool with BS keys per block\n"
                          "(blocks scattered by a seeded permutation); 0: the static cache")
+    ap.add_argument("--heads", action="store_true",
+                    help="time the merged LM head (and the merged embedding sum) of the\n"
+                         "workload's batch instead of the attention + sampling step")
     ap.add_argument("--eager", action="store_true",
                     help="run warmup + steps eager steps (no graph, no timing) and exit;\n"
                          "the launch sequence the hardware-counter runs profile")
@@ -81,6 +84,76 @@ def counter_traffic(workload):
     if rec.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None, "kernel sources changed since the counters were taken"
     return rec, "counters match the current kernel sources"
+
+
+def heads_bench(a, w):
+    """The merged 9-codebook LM head [B, D] x [9 x 1089, D] on the last position (and the
+    merged embedding sum), each timed as a captured graph of back-to-back launches over
+    rotating weight sets."""
+    import numpy as np
+    import torch
+    import autoregressive_audio_token_amd as dec
+    from workloads import configs, gen, device as wdev
+
+    dev = torch.device("cuda:0")
+    D, B, n_cb = configs.D_MODEL, w.batch, w.n_codebooks
+    V, S = w.vocab_valid, w.vocab_stride
+    alg = n_cb * V * D * 2 + B * D * 2 + B * n_cb * V * 4       # W valid rows, h, logits
+    w_alloc = n_cb * S * D * 2
+    R = max(2, math.ceil((1 << 30) / w_alloc))
+    h = wdev.to_device(gen.hidden(w, D), dev)
+    W0 = wdev.to_device(gen.lm_head_weights(w, D), dev)
+    Ws = [W0] + [torch.empty_like(W0).copy_(W0) for _ in range(R - 1)]
+    E = wdev.to_device(gen.embedding_table(w, D), dev)
+    toks = torch.from_numpy(np.random.default_rng(1).integers(0, V, (B, n_cb)).astype(np.int32)).to(dev)
+    logits = torch.empty((B, n_cb, S), dtype=torch.float32, device=dev)
+    x = torch.empty((B, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    n_k = max(R, a.kernel_launches)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for i in range(R):
+                fn(i)
+            stream.synchronize()
+            dec.dec_graph_begin(stream)
+            for i in range(n_k):
+                fn(i)
+            g = dec.dec_graph_end(stream)
+            dec.dec_graph_launch(g, stream)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            dec.dec_graph_launch(g, stream)
+        e1.record(stream)
+        stream.synchronize()
+        dec.dec_graph_destroy(g)
+        return e0.elapsed_time(e1) * 1e3 / (3 * n_k)
+
+    head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
+    emb_us = timed(lambda i: dec.dec_embed_sum(toks, E, x, B, n_cb, S, D, stream))
+    ok = bool(torch.isfinite(logits[:, :, :V]).all().item() and torch.isfinite(x).all().item())
+    achieved = alg / (head_us * 1e-6) / 1e9
+    result = {
+        "metric": "merged LM head: algorithmic HBM GB/s (weights, hidden state, logits)",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": 3 * n_k,
+        "warmup": n_k, "ms_per_step": round(head_us * 1e-3, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "d_model": D, "codebooks": n_cb,
+                   "vocab": V, "vocab_stride": S, "weight_sets": R,
+                   "algorithmic_bytes_per_launch": alg},
+        "roofline": {"bound": "hbm", "kernel": "lm_head_kernel (dec_lm_head)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(head_us, 3),
+                     "avg_launch_us_method": f"HIP events around a captured graph of {n_k} "
+                                             f"launches, 3 replays"},
+        "embed_sum_us": round(emb_us, 3),
+        "checks": {"outputs_finite": ok},
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
 
 
 def copy_calibration(mib):
@@ -167,6 +240,8 @@ def main(argv=None):
     from workloads import configs, gen, device as wdev
 
     w = configs.BY_NAME[a.workload]
+    if a.heads:
+        return heads_bench(a, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s_len, c_len = gen.lengths(w)

@@ -212,6 +212,32 @@ int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   const int32_t* len, int n_layers, int B, int H, int L_cap, int hd, int dtype,
                   dec_stream_t stream);
 
+/* The merged 9-codebook LM head on the last position ("Analysis and
+ * improvements": logits only for the last position; the nine heads merged into
+ * one weight matrix):
+ *   logits[b, c, v] = sum_d h[b, d] * W[c, v, d]     for v < V_valid
+ *   h       [B, D] bf16              the decoder's last hidden state
+ *   W       [n_cb, V_stride, D] bf16 rows v >= V_valid are never read
+ *   logits  [B, n_cb, V_stride] fp32 (the dec_sample_topk input); columns
+ *           v >= V_valid are left untouched
+ * No bias.  fp32 accumulation.  D one of 512, 768, 1024, 1536, 2048, else
+ * DEC_E_UNSUPPORTED; h and W 16-byte aligned.  Device pointers, caller-owned. */
+int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n_cb,
+                int V_valid, int V_stride, dec_stream_t stream);
+
+/* The merged 9-codebook embedding lookup: the decoder input of the next step
+ * is the sum of the codebooks' embedding rows ("Analysis and improvements":
+ * nine lookups merged into one; "A rough architecture of Parler TTS": all nine
+ * tokens of a step enter together):
+ *   x[b, d] = sum_c E[c, tokens[b, c], d]   (codebook order, fp32)
+ *   tokens [B, n_cb] int32; a token outside [0, V_emb) adds nothing (the fill
+ *          token needs a row of its own to contribute)
+ *   E      [n_cb, V_emb, D] bf16, 16-byte aligned, D a multiple of 8
+ *   x      [B, D] fp32, 16-byte aligned
+ * B <= 65535.  Device pointers, caller-owned. */
+int dec_embed_sum(const int32_t* tokens, const void* E, float* x, int B, int n_cb, int V_emb,
+                  int D, dec_stream_t stream);
+
 /* Advance device-resident decode state by one step inside a captured graph:
  * len[b] += 1 (if len != NULL) and step[b] += 1 (if step != NULL) for b < B. */
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);

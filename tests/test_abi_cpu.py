@@ -164,6 +164,36 @@ def test_paged_attention_host_validation():
     assert st == D.DEC_E_UNSUPPORTED
 
 
+@_no_gpu
+def test_heads_host_validation():
+    def head(**kw):
+        a = dict(h=A, W=A, lg=A, B=1, D=1024, ncb=9, V=1089, S=1096)
+        a.update(kw)
+        return D.raw_status("dec_lm_head", a["h"], a["W"], a["lg"], a["B"], a["D"], a["ncb"],
+                            a["V"], a["S"], None)
+    for k in ("h", "W", "lg"):
+        assert head(**{k: None}) == D.DEC_E_NULL, k
+    for bad in (dict(B=0), dict(ncb=0), dict(V=0), dict(S=1000), dict(D=0)):
+        assert head(**bad) == D.DEC_E_SHAPE, bad
+    for bad in (dict(D=1000), dict(D=4096), dict(D=64)):
+        assert head(**bad) == D.DEC_E_UNSUPPORTED, bad
+    assert head(h=A + 8) == D.DEC_E_ALIGN and head(W=A + 4) == D.DEC_E_ALIGN
+    assert head(lg=A + 2) == D.DEC_E_ALIGN
+
+    def emb(**kw):
+        a = dict(t=A, E=A, x=A, B=1, ncb=9, V=1096, D=1024)
+        a.update(kw)
+        return D.raw_status("dec_embed_sum", a["t"], a["E"], a["x"], a["B"], a["ncb"], a["V"],
+                            a["D"], None)
+    for k in ("t", "E", "x"):
+        assert emb(**{k: None}) == D.DEC_E_NULL, k
+    for bad in (dict(B=0), dict(B=65536), dict(ncb=0), dict(V=0), dict(D=0)):
+        assert emb(**bad) == D.DEC_E_SHAPE, bad
+    assert emb(D=1020) == D.DEC_E_UNSUPPORTED
+    assert emb(t=A + 2) == D.DEC_E_ALIGN and emb(E=A + 8) == D.DEC_E_ALIGN
+    assert emb(x=A + 4) == D.DEC_E_ALIGN
+
+
 def _samp_rng(**kw):
     a = dict(lg=A, B=1, ncb=9, V=1089, S=1096, T=A, k=50, seed=7, step=None, fill=1089, tok=A,
              idx=None, prob=None)

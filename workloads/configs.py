@@ -81,6 +81,8 @@ STREAM_Q_SELF, STREAM_K_SELF, STREAM_V_SELF = 0, 1, 2
 STREAM_Q_CROSS, STREAM_K_CROSS, STREAM_V_CROSS = 3, 4, 5
 STREAM_LENGTHS, STREAM_LOGITS, STREAM_UNIFORMS, STREAM_TEMPERATURE = 6, 7, 8, 9
 STREAM_K_NEW, STREAM_V_NEW = 10, 11           # the current token's key/value rows per step
+STREAM_HIDDEN, STREAM_LM_W, STREAM_EMBED = 12, 13, 14   # LM head input / weights, embeddings
+D_MODEL = 1024                 # decoder width (24 layers x 16 heads x 64)
 
 
 def valid_kv_bytes(w: Workload, self_lens, cross_lens) -> int:

@@ -27,7 +27,8 @@ import numpy as np
 from .configs import (SEED_ROOT, STREAM_Q_SELF, STREAM_K_SELF, STREAM_V_SELF,
                       STREAM_Q_CROSS, STREAM_K_CROSS, STREAM_V_CROSS,
                       STREAM_LENGTHS, STREAM_LOGITS, STREAM_UNIFORMS,
-                      STREAM_TEMPERATURE, STREAM_K_NEW, STREAM_V_NEW, Workload)
+                      STREAM_TEMPERATURE, STREAM_K_NEW, STREAM_V_NEW, STREAM_HIDDEN,
+                      STREAM_LM_W, STREAM_EMBED, Workload)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -136,6 +137,25 @@ def new_rows(w: Workload, which: str, step: int = 0):
     stream = STREAM_K_NEW if which == "k" else STREAM_V_NEW
     return _normals(rng_for(w.cfg_id, stream, 0, 0, step),
                     (w.n_layers, w.batch, w.heads, w.head_dim), w.qkv_std, w.dtype)
+
+
+def hidden(w: Workload, D: int, step: int = 0):
+    """The decoder's last hidden state at the last position: [B, D] bf16 bits, N(0,1)."""
+    return _normals(rng_for(w.cfg_id, STREAM_HIDDEN, 0, 0, step), (w.batch, D), 1.0, "bf16")
+
+
+def lm_head_weights(w: Workload, D: int):
+    """Merged LM head [n_codebooks, vocab_stride, D] bf16 bits, N(0,1)/sqrt(D) (so logits
+    are O(1)); padding rows are drawn too (the head never reads them)."""
+    return _normals(rng_for(w.cfg_id, STREAM_LM_W), (w.n_codebooks, w.vocab_stride, D),
+                    1.0 / 32 if D == 1024 else float(D) ** -0.5, "bf16")
+
+
+def embedding_table(w: Workload, D: int):
+    """Merged embeddings [n_codebooks, vocab_stride, D] bf16 bits, N(0,1)/8 (rows for
+    every valid token and the fill token)."""
+    return _normals(rng_for(w.cfg_id, STREAM_EMBED), (w.n_codebooks, w.vocab_stride, D),
+                    0.125, "bf16")
 
 
 def logits(w: Workload, step: int = 0, pad_value=1e30):
