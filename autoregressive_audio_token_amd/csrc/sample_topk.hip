@@ -86,34 +86,74 @@ __device__ __forceinline__ bool search2(const uint32_t (&key)[NS], int kk, int l
   return false;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Radix search for tau over NS slots per lane (absent slots: idx -1).  Every present
+// key lies in [lo, hi], so the bits above the highest bit where lo and hi differ are
+// shared and known.  Each pass resolves the next 8 bits: the keys that still match
+// the resolved prefix are counted into 256 LDS buckets (stored in descending bucket
+// order, so lane l holds buckets 255-4l..252-4l in one 16-byte read), a wave scan
+// turns the counts into "keys at or above this bucket", and a ballot picks the
+// bucket that holds the kk-th largest key.  Returns tau such that either exactly kk
+// keys are >= tau (an exact cut was found), or tau is the kk-th largest key; both
+// give the same kept set under the tie rule of select_kept.
+template <int NS>
+__device__ __forceinline__ uint32_t radix_tau(const uint32_t (&key)[NS], const int (&idx)[NS],
+                                              int kk, uint32_t lo, uint32_t hi, uint32_t* hist) {
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0u) return hi;
+  const int lane = static_cast<int>(__lane_id());
+  int top = 31 - __builtin_clz(diff);                          // highest unresolved bit
+  uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
+  int above = 0;                                               // keys above the prefix range
+  u32x4_t* h4 = reinterpret_cast<u32x4_t*>(hist);
+  for (;;) {
+    const int sh = top >= 7 ? top - 7 : 0;
+    const uint32_t high = top == 31 ? 0u : ~((2u << top) - 1u);  // resolved bits
+    h4[lane] = u32x4_t{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      if (idx[j] >= 0 && (key[j] & high) == prefix)
+        atomicAdd(&hist[255 - ((key[j] >> sh) & 0xFFu)], 1u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4_t c4 = h4[lane];
+    const int a0 = (int)c4.x, a1 = a0 + (int)c4.y, a2 = a1 + (int)c4.z, a3 = a2 + (int)c4.w;
+    const int base = wave_exclusive_sum_int(a3, lane);
+    const int need = kk - above;
+    const unsigned long long reach = __ballot(base + a3 >= need);
+    const int L = __ffsll((long long)reach) - 1;   // a lane reaches need: candidates >= need
+    const int bL = __builtin_amdgcn_readlane(base, L);
+    const int r0 = bL + __builtin_amdgcn_readlane(a0, L);
+    const int r1 = bL + __builtin_amdgcn_readlane(a1, L);
+    const int r2 = bL + __builtin_amdgcn_readlane(a2, L);
+    const int r3 = bL + __builtin_amdgcn_readlane(a3, L);
+    const int i = r0 >= need ? 0 : r1 >= need ? 1 : r2 >= need ? 2 : 3;
+    const int cum_at = i == 0 ? r0 : i == 1 ? r1 : i == 2 ? r2 : r3;
+    const int cum_before = i == 0 ? bL : i == 1 ? r0 : i == 2 ? r1 : r2;
+    // bits above `top` inside the 8-bit digit (only when sh == 0) equal the prefix's
+    prefix |= (uint32_t)(255 - (4 * L + i)) << sh;
+    if (cum_at == need) return prefix;  // exactly kk keys are >= prefix
+    above += cum_before;
+    if (sh == 0) return prefix;         // every bit resolved: the kk-th largest key
+    top = sh - 1;
+  }
+}
+
 // Exact top-kk over NS slots per lane whose slot-major order is vocabulary order.
 // Absent slots carry key 0 and idx -1.  Every present key is at least `lo`, and
-// the largest is `hi`, so the search starts below their common leading bits.
-// Writes the kept (value, index) pairs in vocabulary order to cval/cidx[0..kk)
-// (lanes outside the kept set write a dummy slot, so no store is predicated).
+// the largest is `hi`.  Writes the kept (value, index) pairs in vocabulary order to
+// cval/cidx[0..kk) (lanes outside the kept set write a dummy slot, so no store is
+// predicated).  hist: 256 words of this wave's LDS, 16-byte aligned.
 template <int NS>
 __device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const int (&idx)[NS], int kk,
-                                            uint32_t lo, uint32_t hi, float* cval, int* cidx) {
-  // tau: the largest t with #(key >= t) >= kk (the kk-th largest key), or the
-  // first t at which exactly kk keys are >= t; both give the same kept set
-  const uint32_t diff = lo ^ hi;
-  uint32_t tau = hi;
-  if (diff != 0u) {
-    const int top = 31 - __builtin_clz(diff);
-    tau = top == 31 ? 0u : (hi & ~((2u << top) - 1u));  // the shared leading bits
-    int bit = top;
-    bool done = false;
-    if ((bit & 1) == 0) {  // an odd number of bits to resolve: one single-bit step first
-      const uint32_t cand = tau | (1u << bit);
-      const int cnt = count_ge(key, cand);
-      if (cnt >= kk) {
-        tau = cand;
-        done = cnt == kk;
-      }
-      --bit;
-    }
-    for (; !done && bit > 0; bit -= 2) done = search2(key, kk, bit - 1, tau);
-  }
+                                            uint32_t lo, uint32_t hi, float* cval, int* cidx,
+                                            uint32_t* hist) {
+  const uint32_t tau = radix_tau(key, idx, kk, lo, hi, hist);
   int cnt_gt = 0;
 #pragma unroll
   for (int j = 0; j < NS; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
@@ -162,6 +202,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   __shared__ float s_val[kSampWaves][2 * kWave];
   __shared__ int s_idx[kSampWaves][2 * kWave];
   __shared__ uint2 s_surv[kSampWaves][kSurvCap + kWave];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSampWaves][256];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -240,9 +281,9 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
       sk[j] = q < nsurv ? e.x : 0u;
       si[j] = q < nsurv ? (int)e.y : -1;
     }
-    select_kept(sk, si, kk, thr, kmax, s_val[wave], s_idx[wave]);
+    select_kept(sk, si, kk, thr, kmax, s_val[wave], s_idx[wave], s_hist[wave]);
   } else {  // too many survivors (heavy ties or a flat row): search the whole row
-    select_kept(key, idx, kk, 0u, kmax, s_val[wave], s_idx[wave]);
+    select_kept(key, idx, kk, 0u, kmax, s_val[wave], s_idx[wave], s_hist[wave]);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
