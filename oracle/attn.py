@@ -77,3 +77,26 @@ def attention(q, K, V, lens, scale, dtype):
     NL, B, H, hd = q.shape
     rows = [(layer, b, h) for layer in range(NL) for b in range(B) for h in range(H)]
     return attention_rows(q, K, V, lens, scale, dtype, rows).reshape(NL, B, H, hd)
+
+
+def attend_masked(q, K, V, n, mask, scale):
+    """Attention of ``q`` over the keys j < n with ``mask[j]`` true (a boolean mask
+    over the description; "A rough architecture of Parler TTS": cross-attention reads
+    the encoded description, whose padding an attention mask hides).  No key
+    attended: zeros.  All arguments are float64 values except the boolean mask."""
+    hd = q.shape[-1]
+    n = min(int(n), K.shape[0])
+    keep = np.nonzero(np.asarray(mask[:max(n, 0)], dtype=bool))[0]
+    if keep.size == 0:
+        return np.zeros(hd, dtype=np.float64)
+    s = scale * (K[keep] @ q)
+    w = np.exp(s - s.max())
+    return (w @ V[keep]) / w.sum()
+
+
+def round_bf16(x):
+    """float32 values rounded to bfloat16 (nearest, ties to even), returned as float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)) << np.uint32(16)
+    return r.astype(np.uint32).view(np.float32)

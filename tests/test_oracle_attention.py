@@ -202,3 +202,46 @@ def test_rows_subset_matches_full():
     rows = [(0, 0, 3), (0, 0, 1)]
     part = A.attention_rows(q, K, V, s_len, w.scale, w.dtype, rows)
     assert np.array_equal(part[0], full[0, 0, 3]) and np.array_equal(part[1], full[0, 0, 1])
+
+
+def test_masked_attention_closed_forms_and_reductions():
+    import math
+    from oracle import attn as oa
+    rng = np.random.default_rng(21)
+    L, hd = 12, 8
+    q = rng.standard_normal(hd)
+    K = rng.standard_normal((L, hd))
+    V = rng.standard_normal((L, hd))
+    full = np.ones(L, bool)
+    # all true: plain attention over the prefix
+    for n in (1, 5, 12):
+        assert np.allclose(oa.attend_masked(q, K, V, n, full, 0.3), oa.attend_one(q, K, V, n, 0.3))
+    # a prefix mask equals a shorter length
+    m = np.zeros(L, bool); m[:4] = True
+    assert np.allclose(oa.attend_masked(q, K, V, 10, m, 0.3), oa.attend_one(q, K, V, 4, 0.3))
+    # one attended key returns its value; none returns zeros; keys past n never count
+    m = np.zeros(L, bool); m[7] = True
+    assert np.array_equal(oa.attend_masked(q, K, V, 12, m, 0.3), V[7])
+    assert not oa.attend_masked(q, K, V, 7, m, 0.3).any()
+    # brute force with fsum over a scattered mask
+    m = rng.random(L) < 0.5; m[2] = True
+    keep = [j for j in range(9) if m[j]]
+    s = [0.3 * math.fsum(q[d] * K[j, d] for d in range(hd)) for j in keep]
+    mx = max(s); w = [math.exp(x - mx) for x in s]; Z = math.fsum(w)
+    want = [math.fsum(w[i] * V[j, d] for i, j in enumerate(keep)) / Z for d in range(hd)]
+    assert np.allclose(oa.attend_masked(q, K, V, 9, m, 0.3), want, rtol=1e-12, atol=1e-14)
+    # permuting the keys together with the mask changes nothing
+    p = rng.permutation(L)
+    assert np.allclose(oa.attend_masked(q, K[p], V[p], L, m[p], 0.3),
+                       oa.attend_masked(q, K, V, L, m, 0.3))
+
+
+def test_round_bf16_matches_generator_rounding_and_ties():
+    from oracle import attn as oa
+    from workloads import gen
+    x = np.random.default_rng(3).standard_normal(1000).astype(np.float32) * 100
+    bits = gen.f32_to_bf16_bits(x)
+    assert np.array_equal(oa.round_bf16(x).view(np.uint32), bits.astype(np.uint32) << 16)
+    # ties to even: 1 + 2^-8 lies halfway between bf16 1 and 1 + 2^-7; even is 1
+    assert oa.round_bf16(np.float32(1 + 2 ** -8)) == np.float32(1.0)
+    assert oa.round_bf16(np.float32(1 + 3 * 2 ** -8)) == np.float32(1 + 2 ** -6)
