@@ -169,6 +169,8 @@ __device__ __forceinline__ int group_items(int n, int NLH, int cpi) {
 
 // Fold chunk state (mc, lc, ac) into the running state (m, l, a); the first
 // chunk initialises it.  Shared by both fold sites so they agree bit for bit.
+// EX (key masks): a chunk may have no attended key (mc = -inf) and is skipped.
+template <bool EX>
 __device__ __forceinline__ void fold_chunk(bool first, float mc, float lc, float ac, float& m,
                                            float& l, float& a) {
   if (first) {
@@ -177,6 +179,7 @@ __device__ __forceinline__ void fold_chunk(bool first, float mc, float lc, float
     a = ac;
     return;
   }
+  if (EX && mc == -INFINITY) return;
   const float mn = fmaxf(m, mc);
   const float fa = exp2_hw(m - mn);
   const float fc = exp2_hw(mc - mn);
@@ -212,14 +215,18 @@ struct Tile {
   }
 
   // Online-softmax update of this lane group's state (m, l, acc) with the tile.
+  // MASK: bit j of `keep` says whether key base + j is attended (a boolean key mask).
+  template <bool MASK = false>
   __device__ __forceinline__ void consume(const QSlice<T>& qs, int base, int n, int kg,
-                                          float& m, float& l, float (&acc)[EPL]) const {
+                                          float& m, float& l, float (&acc)[EPL],
+                                          uint64_t keep = ~0ull) const {
     float s[NLD];
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       s[i] = qs.finish(group_sum<LPK>(qs.dot(k[i])));
       if (base + i * KPL + kg >= n) s[i] = -INFINITY;
+      if (MASK && ((keep >> (i * KPL + kg)) & 1ull) == 0ull) s[i] = -INFINITY;
       tmax = fmaxf(tmax, s[i]);
     }
     if (tmax == -INFINITY) return;  // no valid key of this group in the tile
@@ -238,15 +245,37 @@ struct Tile {
   }
 };
 
-// Buffer descriptors for one tile's K and V rows, and the tile's first row inside them.
+// Buffer descriptors for one tile's K and V rows, the tile's first row inside them,
+// and (key masks) which of its keys are attended.
 struct TileAddr {
   __amdgpu_buffer_rsrc_t k, v;
   int row0;
+  uint64_t keep;
 };
+
+// An output element a / l.  EX: fp32 or bfloat16 (rounded to nearest even), and zero
+// for a sequence with no attended key (l == 0, only under a key mask).
+template <bool EX>
+__device__ __forceinline__ void store_out(const AttnSeg& S, size_t i, float a, float l) {
+  if (!EX) {
+    static_cast<float*>(S.out)[i] = a / l;
+    return;
+  }
+  const float v = l > 0.f ? a / l : 0.f;
+  if (S.out_bf16) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    static_cast<uint16_t*>(S.out)[i] = (uint16_t)r;
+  } else {
+    static_cast<float*>(S.out)[i] = v;
+  }
+}
 
 // PAGED: segments with a block table read each tile through a descriptor over its block of
 // the pool (a 64-key tile never crosses a block); other segments read the static layout.
-template <typename T, bool PAGED>
+// EX: the widened entry point -- segments with a key bitmask skip the keys whose bit
+// is clear, and outputs may be bf16.
+template <typename T, bool PAGED, bool EX = false>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p) {
   constexpr int HD = kAttnHeadDim;
   using TileT = Tile<T>;
@@ -403,7 +432,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const size_t slot_sidx = ((size_t)(slh / p.H) * B + b) * p.H + (slh % p.H);
 
     if (n == 0) {  // no valid key: defined output of zeros
-      if (slot_ok) S.out[slot_sidx * HD + d] = 0.f;
+      if (slot_ok) {
+        if (EX) store_out<EX>(S, slot_sidx * HD + d, 0.f, 0.f);
+        else static_cast<float*>(S.out)[slot_sidx * HD + d] = 0.f;
+      }
       continue;
     }
 
@@ -445,8 +477,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           const int base = cb + t * kStep;
           // past this wave's tiles of the chunk: a descriptor with no rows, so the
           // pipeline's last prefetch moves no bytes (the next chunk loads its own)
-          if (t >= nt) return {rk_none, rv_none, 0};
-          if (!paged) return {rk_seq, rv_seq, base};
+          if (t >= nt) return {rk_none, rv_none, 0, 0ull};
+          uint64_t keep = ~0ull;
+          if (EX && S.mask != nullptr)  // the tile's 64 mask bits (two words, uniform)
+            keep = *reinterpret_cast<const uint64_t*>(S.mask + (size_t)b * S.mask_words +
+                                                      (base >> 5));
+          if (!paged) return {rk_seq, rv_seq, base, keep};
           const int bs = 1 << S.bs_log2;
           const int row = base & (bs - 1);
           const int blk = __builtin_amdgcn_readlane(blk_of, t);
@@ -454,11 +490,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           int rows = base < n ? min(bs - row, n - base) : 0;
           if (blk < 0 || blk >= S.n_blocks) rows = 0;
           const size_t off = (((head_off + (size_t)(unsigned)blk) * p.H + (wlh % p.H)) * bs + row) * HD;
-          return {rows_rsrc(kp + off, rows, kRowBytes), rows_rsrc(vp + off, rows, kRowBytes), 0};
+          return {rows_rsrc(kp + off, rows, kRowBytes), rows_rsrc(vp + off, rows, kRowBytes), 0,
+                  keep};
         };
         TileT ta, tb;
         const TileAddr a0 = addr(0);
         ta.load(a0.k, a0.v, a0.row0, lane_off);
+        uint64_t keep_a = a0.keep;
         QSlice<T> qs;  // after the first tile's loads, so K/V requests leave first
         qs.load(qp, p.qscale);
         // ping-pong: the next tile is in flight while one is consumed (past n the
@@ -468,11 +506,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           const int base = cb + t * kStep;
           const TileAddr a1 = addr(t + 1);
           tb.load(a1.k, a1.v, a1.row0, lane_off);
-          ta.consume(qs, base, n, kg, m_g, l_g, acc);
+          ta.template consume<EX>(qs, base, n, kg, m_g, l_g, acc, keep_a);
           if (t + 1 >= nt) break;
           const TileAddr a2 = addr(t + 2);
           ta.load(a2.k, a2.v, a2.row0, lane_off);
-          tb.consume(qs, base + kStep, n, kg, m_g, l_g, acc);
+          tb.template consume<EX>(qs, base + kStep, n, kg, m_g, l_g, acc, a1.keep);
+          keep_a = a2.keep;
         }
       }
       // merge the lane groups of the wave, in butterfly order
@@ -502,7 +541,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           ac = fmaf(fw, s_acc[w][d], ac);
         }
         if (whole) {
-          fold_chunk(c == c0, mc, lc, ac, fm, fl, fa);
+          fold_chunk<EX>(c == c0, mc, lc, ac, fm, fl, fa);
         } else {  // publish the chunk state, write-through
           float* pp = S.part + (slot_sidx * S.nck_cap + c) * kAttnPartStride;
           __hip_atomic_store(pp + 4 + d, ac, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -515,7 +554,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       __syncthreads();  // LDS is rewritten by the next chunk
     }
     if (whole) {
-      if (slot_ok) S.out[slot_sidx * HD + d] = fa / fl;
+      if (slot_ok) store_out<EX>(S, slot_sidx * HD + d, fa, fl);
       continue;
     }
     // split mode (one chunk per item): every thread's stores have completed before
@@ -536,9 +575,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           const float mc = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const float lc = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const float ac = __hip_atomic_load(q + 4 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          fold_chunk(cc == 0, mc, lc, ac, fm, fl, fa);
+          fold_chunk<EX>(cc == 0, mc, lc, ac, fm, fl, fa);
         }
-        S.out[slot_sidx * HD + d] = fa / fl;
+        store_out<EX>(S, slot_sidx * HD + d, fa, fl);
       }
       if (tid == 0)
         __hip_atomic_store(S.ticket + slot_sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -560,22 +599,37 @@ long long attn_items_cap(const AttnParams& p) {
 namespace {
 struct DevInfo {
   int cus = 0;
-  int occ[2][2] = {{0, 0}, {0, 0}};  // resident workgroups per CU [dtype][paged], small LDS
+  int occ[2][3] = {{0, 0, 0}, {0, 0, 0}};  // resident workgroups per CU [dtype][variant]
 };
 DevInfo g_dev[64];
 }  // namespace
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, bool EX>
 static void* attn_kernel_ptr() {
-  return reinterpret_cast<void*>(&attn_decode_kernel<T, PAGED>);
+  return reinterpret_cast<void*>(&attn_decode_kernel<T, PAGED, EX>);
+}
+
+template <typename T, bool PAGED, bool EX>
+static void attn_kernel_go(int blocks, size_t lds, hipStream_t stream, const AttnParams& p) {
+  hipLaunchKernelGGL((attn_decode_kernel<T, PAGED, EX>), dim3(blocks), dim3(kAttnThreads), lds,
+                     stream, p);
 }
 
 hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream) {
   const int G = p.nseg * p.B;
   const size_t lds = (size_t)(3 * G + 1) * sizeof(int);
   const bool paged = p.seg[0].table != nullptr || (p.nseg > 1 && p.seg[1].table != nullptr);
-  void* fn = dtype == 0 ? (paged ? attn_kernel_ptr<uint16_t, true>() : attn_kernel_ptr<uint16_t, false>())
-                        : (paged ? attn_kernel_ptr<float, true>() : attn_kernel_ptr<float, false>());
+  const bool ex = p.seg[0].mask != nullptr || p.seg[0].out_bf16 ||
+                  (p.nseg > 1 && (p.seg[1].mask != nullptr || p.seg[1].out_bf16));
+  // instantiations: static, paged, widened (key masks / bf16 outputs, static caches)
+  const int variant = ex ? 2 : paged ? 1 : 0;
+  void* fn = dtype == 0
+                 ? (variant == 2 ? attn_kernel_ptr<uint16_t, false, true>()
+                    : variant == 1 ? attn_kernel_ptr<uint16_t, true, false>()
+                                   : attn_kernel_ptr<uint16_t, false, false>())
+                 : (variant == 2 ? attn_kernel_ptr<float, false, true>()
+                    : variant == 1 ? attn_kernel_ptr<float, true, false>()
+                                   : attn_kernel_ptr<float, false, false>());
   if (blocks <= 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -587,26 +641,26 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
       if (e != hipSuccess) return e;
       di.cus = cus;
     }
-    int occ = di.occ[dtype][paged ? 1 : 0];
+    int occ = di.occ[dtype][variant];
     if (occ == 0 || G > 64) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);
       if (e != hipSuccess) return e;
       if (occ < 1) occ = 1;
-      if (G <= 64) di.occ[dtype][paged ? 1 : 0] = occ;
+      if (G <= 64) di.occ[dtype][variant] = occ;
     }
     const long long cap = attn_items_cap(p);
     const long long want = (long long)di.cus * occ;
     blocks = (int)(want < cap ? want : cap);
   }
   if (blocks < 1) blocks = 1;
-  if (dtype == 0 && !paged) {
-    hipLaunchKernelGGL((attn_decode_kernel<uint16_t, false>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
-  } else if (dtype == 0) {
-    hipLaunchKernelGGL((attn_decode_kernel<uint16_t, true>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
-  } else if (!paged) {
-    hipLaunchKernelGGL((attn_decode_kernel<float, false>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+  if (dtype == 0) {
+    if (variant == 2) attn_kernel_go<uint16_t, false, true>(blocks, lds, stream, p);
+    else if (variant == 1) attn_kernel_go<uint16_t, true, false>(blocks, lds, stream, p);
+    else attn_kernel_go<uint16_t, false, false>(blocks, lds, stream, p);
   } else {
-    hipLaunchKernelGGL((attn_decode_kernel<float, true>), dim3(blocks), dim3(kAttnThreads), lds, stream, p);
+    if (variant == 2) attn_kernel_go<float, false, true>(blocks, lds, stream, p);
+    else if (variant == 1) attn_kernel_go<float, true, false>(blocks, lds, stream, p);
+    else attn_kernel_go<float, false, false>(blocks, lds, stream, p);
   }
   return hipGetLastError();
 }

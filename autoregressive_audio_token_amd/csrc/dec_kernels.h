@@ -38,7 +38,7 @@ struct AttnSeg {
   const void* k;          // [NL, B, H, L_cap, 64]
   const void* v;          // [NL, B, H, L_cap, 64]
   const int32_t* len;     // [B] valid slots
-  float* out;             // [NL, B, H, 64]
+  void* out;              // [NL, B, H, 64] fp32, or bf16 when out_bf16
   float* part;            // [NL*B*H, nck_cap, kAttnPartStride] chunk partials (split mode)
   int32_t* ticket;        // [NL*B*H] chunk arrival counters (split mode), zero between calls
   int L_cap;              // keys a sequence can hold (paged: table_stride << bs_log2)
@@ -48,6 +48,10 @@ struct AttnSeg {
   int table_stride;
   int n_blocks;           // physical blocks per layer
   int bs_log2;            // log2(keys per block), at least log2(64)
+  // key mask (mask != nullptr): bit j % 32 of word j / 32 of row b set = key j attended
+  const uint32_t* mask;   // [B, mask_words], mask_words even
+  int mask_words;
+  int out_bf16;
 };
 
 struct AttnParams {

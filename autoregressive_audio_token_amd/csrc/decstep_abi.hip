@@ -60,13 +60,17 @@ struct SegArgs {
   const void* k;
   const void* v;
   const int32_t* len;
-  float* out;
+  void* out;
   int L_cap;
   // paged cache: k, v are block pools; L_cap = table_stride * block_size
   const int32_t* table = nullptr;
   int table_stride = 0;
   int n_blocks = 0;
   int block_size = 0;
+  // key bitmask [B, mask_words] (bit j % 32 of word j / 32: key j attended), or none
+  const uint32_t* mask = nullptr;
+  int mask_words = 0;
+  int out_bf16 = 0;
 };
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -96,8 +100,15 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   if (nseg * B > dec::kAttnMaxGroups) return DEC_E_UNSUPPORTED;
   for (int s = 0; s < nseg; ++s) {
     if (!aligned(segs[s].q, 16) || !aligned(segs[s].k, 16) || !aligned(segs[s].v, 16) ||
-        !aligned(segs[s].len, 4) || !aligned(segs[s].out, 4))
+        !aligned(segs[s].len, 4) || !aligned(segs[s].out, segs[s].out_bf16 ? 2 : 4))
       return DEC_E_ALIGN;
+    if (segs[s].mask != nullptr) {
+      // every 64-key tile reads two whole words
+      const long long need = 2LL * ((segs[s].L_cap + 63) / 64);
+      if (segs[s].mask_words < need || segs[s].mask_words % 2 != 0) return DEC_E_SHAPE;
+      if (segs[s].table != nullptr) return DEC_E_UNSUPPORTED;  // masks go with static caches
+      if (!aligned(segs[s].mask, 8)) return DEC_E_ALIGN;
+    }
   }
   size_t need = 0;
   SegLayout lay[2];
@@ -132,6 +143,9 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.table_stride = segs[s].table_stride;
     g.n_blocks = segs[s].n_blocks;
     g.bs_log2 = segs[s].table ? __builtin_ctz((unsigned)segs[s].block_size) : 0;
+    g.mask = segs[s].mask;
+    g.mask_words = segs[s].mask_words;
+    g.out_bf16 = segs[s].out_bf16;
     if (lay[s].bytes > 0) {
       char* base = static_cast<char*>(ws) + off;
       g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
@@ -196,6 +210,23 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self, co
                   size_t ws_bytes, dec_stream_t stream) {
   const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
                         {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_step_ex(const void* q_self, const void* k_self, const void* v_self,
+                     const int32_t* len, int L_cap_self, void* out_self, const void* q_cross,
+                     const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                     const uint32_t* cross_mask, int mask_words, int L_cap_cross,
+                     void* out_cross, int n_layers, int B, int H, int hd, int dtype,
+                     int out_dtype, float scale, void* workspace, size_t ws_bytes,
+                     dec_stream_t stream) {
+  if (out_dtype != DEC_BF16 && out_dtype != DEC_F32) return DEC_E_DTYPE;
+  SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
+                  {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  s[1].mask = cross_mask;
+  s[1].mask_words = mask_words;
+  s[0].out_bf16 = s[1].out_bf16 = out_dtype == DEC_BF16 ? 1 : 0;
   return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
                      reinterpret_cast<hipStream_t>(stream));
 }

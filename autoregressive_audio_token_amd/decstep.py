@@ -53,6 +53,8 @@ _SIGS = {
     "dec_attn_cross": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_attn_step": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P,
                            _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "dec_attn_step_ex": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P,
+                              _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_attn_self_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                  _P, _SZ, _P]),
     "dec_attn_step_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P,
@@ -154,6 +156,16 @@ def dec_attn_step(q_self, k_self, v_self, len, L_cap_self, out_self,
                               _ptr(out_self), _ptr(q_cross), _ptr(k_cross), _ptr(v_cross),
                               _ptr(enc_len), L_cap_cross, _ptr(out_cross), n_layers, B, H, hd,
                               dtype, scale, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dec_attn_step_ex(q_self, k_self, v_self, len, L_cap_self, out_self, q_cross, k_cross,
+                     v_cross, enc_len, cross_mask, mask_words, L_cap_cross, out_cross, n_layers,
+                     B, H, hd, dtype, out_dtype, scale, workspace, ws_bytes, stream=None):
+    _check(_lib.dec_attn_step_ex(_ptr(q_self), _ptr(k_self), _ptr(v_self), _ptr(len),
+                                 L_cap_self, _ptr(out_self), _ptr(q_cross), _ptr(k_cross),
+                                 _ptr(v_cross), _ptr(enc_len), _ptr(cross_mask), mask_words,
+                                 L_cap_cross, _ptr(out_cross), n_layers, B, H, hd, dtype,
+                                 out_dtype, scale, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dec_attn_self_paged(q, k_pool, v_pool, block_table, len, out, n_layers, B, H, hd,

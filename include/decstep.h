@@ -116,6 +116,27 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
                   int n_layers, int B, int H, int hd, int dtype, float scale,
                   void* workspace, size_t ws_bytes, dec_stream_t stream);
 
+/* dec_attn_step with two widenings (both optional):
+ *   cross_mask  [B, mask_words] uint32, or NULL: an arbitrary boolean mask over
+ *               the description ("A rough architecture of Parler TTS": the
+ *               encoded description feeds cross-attention; padding inside it is
+ *               hidden by an attention mask).  Bit j % 32 of word j / 32 of row b
+ *               set = key j attended.  Keys j < enc_len[b] with their bit set
+ *               take part; a row with none outputs zeros.  mask_words must be
+ *               even and at least 2 * ceil(L_cap_cross / 64) (each 64-key tile
+ *               reads two whole words); 8-byte aligned.
+ *   out_dtype   DEC_F32 (float outputs, as dec_attn_step) or DEC_BF16 (outputs
+ *               rounded to bfloat16, nearest-even, from the same fp32 values;
+ *               out pointers 2-byte aligned).
+ * Everything else as dec_attn_step. */
+int dec_attn_step_ex(const void* q_self, const void* k_self, const void* v_self,
+                     const int32_t* len, int L_cap_self, void* out_self, const void* q_cross,
+                     const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                     const uint32_t* cross_mask, int mask_words, int L_cap_cross,
+                     void* out_cross, int n_layers, int B, int H, int hd, int dtype,
+                     int out_dtype, float scale, void* workspace, size_t ws_bytes,
+                     dec_stream_t stream);
+
 /* Self-attention over a PAGED cache ("Future work": paged attention, so a
  * sequence's keys live in fixed-size blocks drawn from a shared pool instead of
  * one preallocated run of L_cap slots).  Same arithmetic as dec_attn_self; only

@@ -194,6 +194,22 @@ def test_heads_host_validation():
     assert emb(x=A + 4) == D.DEC_E_ALIGN
 
 
+@_no_gpu
+def test_attention_ex_host_validation():
+    def ex(**kw):
+        a = dict(mask=A, words=32, Lc=1024, out=A, od=0)
+        a.update(kw)
+        return D.raw_status("dec_attn_step_ex", A, A, A, A, 4096, a["out"], A, A, A, A,
+                            a["mask"], a["words"], a["Lc"], a["out"], 24, 1, 16, 64, 0, a["od"],
+                            ctypes.c_float(0.125), A, 1 << 30, None)
+    assert ex(od=3) == D.DEC_E_DTYPE
+    assert ex(words=30) == D.DEC_E_SHAPE        # fewer than 2 words per 64-key tile
+    assert ex(words=33) == D.DEC_E_SHAPE        # odd
+    assert ex(mask=A + 4) == D.DEC_E_ALIGN      # each tile reads an aligned 64-bit pair
+    assert ex(out=A + 2, od=1) == D.DEC_E_ALIGN  # fp32 outputs need 4-byte alignment
+    assert ex(out=A + 1, od=0) == D.DEC_E_ALIGN  # bf16 outputs need 2-byte alignment
+
+
 def _samp_rng(**kw):
     a = dict(lg=A, B=1, ncb=9, V=1089, S=1096, T=A, k=50, seed=7, step=None, fill=1089, tok=A,
              idx=None, prob=None)
