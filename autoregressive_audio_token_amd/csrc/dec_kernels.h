@@ -71,9 +71,10 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
 
 constexpr int kSampWaves = 4;                       // rows (one per wave) per workgroup
 constexpr int kSampMaxVocab = 4096;
+constexpr int kSampNarrowK = 64;                    // top_k up to this: kept set one per lane
 
 struct SampleParams {
-  const float* logits;
+  const void* logits;     // [B, n_cb, V_stride] fp32, or bf16 when logits_bf16
   const float* temperature;
   const float* uniforms;  // [B, n_cb], or unused when rng != 0
   const int32_t* step;
@@ -83,6 +84,7 @@ struct SampleParams {
   unsigned long long seed;  // Philox key word 0 when rng != 0
   int B, n_cb, V_valid, V_stride, top_k, fill;
   int rng;                  // 1: uniforms from Philox4x64-10 at counter (step, b, c, 0)
+  int logits_bf16;
 };
 
 hipError_t sample_launch(const SampleParams& p, hipStream_t stream);

@@ -29,6 +29,13 @@
 //      ascending vocabulary order (kk <= 64).
 //   4. e_t = exp((x_t - max) / T); wave inclusive scan; C_t = S_t / S_last;
 //      the token is the first kept entry with u < C_t.  T <= 0: greedy.
+//
+// Wide variant (top_k > 64): no pruning (the lane maxima bound only the 64th
+// largest key); the radix search runs over the whole row, and the kept entries
+// stay where they were loaded.  Slot j of every lane holds vocabulary entries
+// 64 j .. 64 j + 63, so the CDF in vocabulary order is one wave scan per slot
+// plus the running total of the slots before it.  Logits may be bf16: each
+// value widens exactly to fp32 before its key is formed.
 #include "dec_common.h"
 #include "dec_kernels.h"
 
@@ -195,7 +202,82 @@ __device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, u
   return c0;
 }
 
+__device__ __forceinline__ float logit_at(const float* x, int i) { return x[i]; }
+__device__ __forceinline__ float logit_at(const uint16_t* x, int i) {
+  return __uint_as_float(static_cast<uint32_t>(x[i]) << 16);
+}
+
+// Wide variant, steps 3 and 4 over the loaded slots (see the file comment).  The
+// kept set is {key > tau} plus the lowest-index entries equal to tau; its t-th
+// entry in vocabulary order goes to output position t.
 template <int VPL>
+__device__ __forceinline__ void sample_wide(const SampleParams& p, int row, const uint32_t (&key)[VPL],
+                                            const int (&idx)[VPL], int kk, uint32_t kmax, float T,
+                                            float u, int started, uint32_t* hist) {
+  const int lane = static_cast<int>(__lane_id());
+  const uint32_t tau = radix_tau(key, idx, kk, 0u, kmax, hist);
+  int cnt_gt = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
+  const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
+  const float m = key_value(kmax);
+  const bool greedy = T <= 0.f;
+  float e[VPL], S[VPL];
+  int pos[VPL];
+  float run = 0.f;  // sum of e over the slots before j
+  int eq_before = 0, kept_before = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const bool eq = idx[j] >= 0 && key[j] == tau;
+    const unsigned long long eqm = __ballot(eq);
+    const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
+    const unsigned long long km = __ballot(kept);
+    pos[j] = kept ? kept_before + lanes_below(km) : -1;
+    e[j] = kept && !greedy ? expf((key_value(key[j]) - m) / T) : 0.f;
+    S[j] = run + wave_inclusive_sum(e[j], lane);
+    run = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S[j]), kWave - 1));
+    eq_before += __popcll(eqm);
+    kept_before += __popcll(km);
+  }
+  // run is now the inclusive sum at the last kept entry (later terms are zeros)
+  const float Z = run;
+  int token = -1;  // the sampled index, before the delay mask
+  if (greedy) {  // the lowest index holding the largest key
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const unsigned long long mk = __ballot(idx[j] >= 0 && key[j] == kmax);
+      if (token < 0 && mk) token = j * kWave + __ffsll(mk) - 1;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const unsigned long long mk = __ballot(pos[j] >= 0 && u < S[j] / Z);
+      if (token < 0 && mk) token = j * kWave + __ffsll(mk) - 1;
+    }
+    if (token < 0) {  // rounding left u >= C_last: the last kept entry
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const unsigned long long mk = __ballot(pos[j] == kk - 1);
+        if (mk) token = j * kWave + __ffsll(mk) - 1;
+      }
+    }
+  }
+  if (lane == 0) p.tokens[row] = started ? token : p.fill;
+  int32_t* oi = p.topk_idx != nullptr ? p.topk_idx + (size_t)row * p.top_k : nullptr;
+  float* op = p.topk_prob != nullptr ? p.topk_prob + (size_t)row * p.top_k : nullptr;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    if (pos[j] < 0) continue;
+    if (oi != nullptr) oi[pos[j]] = idx[j];
+    if (op != nullptr) op[pos[j]] = greedy ? (idx[j] == token ? 1.f : 0.f) : e[j] / Z;
+  }
+  for (int t = kk + lane; t < p.top_k; t += kWave) {
+    if (oi != nullptr) oi[t] = -1;
+    if (op != nullptr) op[t] = 0.f;
+  }
+}
+
+template <int VPL, typename LT, bool WIDE>
 __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleParams p) {
   // per wave: kept entries [0, 64) plus one dummy slot per lane; survivors
   // [0, kSurvCap) plus one dummy slot per lane
@@ -226,14 +308,14 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     u = p.uniforms[row];
   }
 
-  const float* x = p.logits + (size_t)row * p.V_stride;
+  const LT* x = static_cast<const LT*>(p.logits) + (size_t)row * p.V_stride;
   float v[VPL];
   uint32_t key[VPL];
   int idx[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
     const int i = j * kWave + lane;
-    v[j] = x[i < p.V_valid ? i : p.V_valid - 1];
+    v[j] = logit_at(x, i < p.V_valid ? i : p.V_valid - 1);
   }
   uint32_t lmax = 0u;
 #pragma unroll
@@ -245,6 +327,10 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     lmax = key[j] > lmax ? key[j] : lmax;
   }
   const uint32_t kmax = wave_max_key(lmax);
+  if constexpr (WIDE) {
+    sample_wide(p, row, key, idx, kk, kmax, T, u, started, s_hist[wave]);
+    return;
+  }
   // L0: the kk-th largest lane maximum, to its 10 leading bits (a lower bound on
   // the kk-th largest key either way: at least kk lanes hold a key >= L0)
   uint32_t l0 = 0u;
@@ -320,8 +406,15 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
 template <int VPL>
 static hipError_t sample_launch_vpl(const SampleParams& p, hipStream_t stream) {
   const int rows = p.B * p.n_cb;
-  const int blocks = (rows + kSampWaves - 1) / kSampWaves;
-  hipLaunchKernelGGL(sample_topk_kernel<VPL>, dim3(blocks), dim3(kSampWaves * kWave), 0, stream, p);
+  const dim3 grid((rows + kSampWaves - 1) / kSampWaves), block(kSampWaves * kWave);
+  const bool wide = p.top_k > kSampNarrowK;
+  if (p.logits_bf16) {
+    if (wide) hipLaunchKernelGGL((sample_topk_kernel<VPL, uint16_t, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((sample_topk_kernel<VPL, uint16_t, false>), grid, block, 0, stream, p);
+  } else {
+    if (wide) hipLaunchKernelGGL((sample_topk_kernel<VPL, float, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((sample_topk_kernel<VPL, float, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -215,6 +215,25 @@ int dec_sample_topk_philox(const float* logits, int B, int n_cb, int V_valid, in
                            const int32_t* step, int32_t fill_token, int32_t* tokens,
                            int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
 
+/* Widened sampler ("Future work", item 2, as dec_sample_topk).
+ *
+ *   logits        [B, n_cb, V_stride], logits_dtype DEC_F32 (4-byte aligned) or
+ *                 DEC_BF16 (2-byte aligned); a bf16 value widens exactly to
+ *                 float32 and is then treated as dec_sample_topk treats it
+ *   top_k         1..V_valid-or-more: any top_k >= 1 up to 4096 (a row keeps
+ *                 min(top_k, V_valid) entries, so top_k >= V_valid keeps the
+ *                 whole row); topk_idx / topk_prob hold top_k entries per row
+ *   uniforms      [B, n_cb] float32 in [0, 1), or NULL: then row (b, c) draws
+ *                 its uniform from Philox4x64-10 with `seed` exactly as
+ *                 dec_sample_topk_philox does
+ * Rule, outputs, delay mask and device-side behaviour as dec_sample_topk.  For
+ * top_k <= 64 the kernel is dec_sample_topk's; above it the CDF is accumulated
+ * in float32 over the kept entries in vocabulary order, 64 at a time. */
+int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
+                       int V_stride, const float* temperature, int top_k, const float* uniforms,
+                       uint64_t seed, const int32_t* step, int32_t fill_token, int32_t* tokens,
+                       int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
+
 /* Write the current token's key and value rows into the static caches
  * ("Analysis and improvements": caches preallocated at a fixed capacity, so a
  * step writes the next row instead of growing a tensor).

@@ -231,6 +231,30 @@ def test_philox_sampler_host_validation():
     assert _samp_rng(prob=A + 1) == D.DEC_E_ALIGN
 
 
+def _samp_ex(**kw):
+    a = dict(lg=A, dt=0, B=1, ncb=9, V=1089, S=1096, T=A, k=250, u=None, seed=7, step=None,
+             fill=1089, tok=A, idx=None, prob=None)
+    a.update(kw)
+    return D.raw_status("dec_sample_topk_ex", a["lg"], a["dt"], a["B"], a["ncb"], a["V"], a["S"],
+                        a["T"], a["k"], a["u"], ctypes.c_uint64(a["seed"]), a["step"], a["fill"],
+                        a["tok"], a["idx"], a["prob"], None)
+
+
+@_no_gpu
+def test_widened_sampler_host_validation():
+    assert _samp_ex(lg=None) == D.DEC_E_NULL
+    assert _samp_ex(T=None) == D.DEC_E_NULL
+    assert _samp_ex(tok=None) == D.DEC_E_NULL
+    assert _samp_ex(dt=2) == D.DEC_E_DTYPE
+    for bad in (dict(B=0), dict(ncb=0), dict(V=0), dict(S=1000), dict(k=0), dict(k=4097)):
+        assert _samp_ex(**bad) == D.DEC_E_SHAPE, bad
+    assert _samp_ex(V=5000, S=5000) == D.DEC_E_UNSUPPORTED
+    assert _samp_ex(lg=A + 2, dt=1) == D.DEC_E_ALIGN      # fp32 logits: 4-byte aligned
+    assert _samp_ex(lg=A + 1, dt=0) == D.DEC_E_ALIGN      # bf16 logits: 2-byte aligned
+    assert _samp_ex(u=A + 2) == D.DEC_E_ALIGN
+    assert _samp_ex(prob=A + 1) == D.DEC_E_ALIGN
+
+
 def _append(**kw):
     a = dict(kn=A, vn=A, kc=A, vc=A, len=A, NL=24, B=1, H=16, L=4096, hd=64, dt=0)
     a.update(kw)
