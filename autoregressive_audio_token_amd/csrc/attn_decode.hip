@@ -150,16 +150,19 @@ __device__ __forceinline__ int items_per_lh(int n, int cpi) {
 
 // Waves that share one sequence: the smallest power of two covering n keys in one
 // round, or every wave of the workgroup (then the sequence runs in chunk rounds).
-// Shorter sequences are packed kAttnWaves / S to a work item.
+// Shorter sequences are packed kAttnWaves / S to a work item.  At least HD / 64
+// waves: the workgroup's threads combine kAttnThreads / HD sequences at a time.
+template <int HD>
 __device__ __forceinline__ int waves_per_seq(int n) {
-  int s = 1;
-  while (s < kAttnWaves && s * kAttnKeysPerTile < n) s <<= 1;
+  int s = HD / kAttnHeadDim < kAttnWaves ? HD / kAttnHeadDim : kAttnWaves;
+  while (s < kAttnWaves && s * attn_keys_per_tile(HD) < n) s <<= 1;
   return s;
 }
 
 // Work items of a (segment, b) group with n valid keys.
+template <int HD>
 __device__ __forceinline__ int group_items(int n, int NLH, int cpi) {
-  const int S = waves_per_seq(n);
+  const int S = waves_per_seq<HD>(n);
   if (S < kAttnWaves) {
     const int P = kAttnWaves / S;
     return (NLH + P - 1) / P;
@@ -188,13 +191,16 @@ __device__ __forceinline__ void fold_chunk(bool first, float mc, float lc, float
   m = mn;
 }
 
-// One wave's view of a tile: NLD loads per operand, each covering KPL keys.
-template <typename T>
+// One wave's view of a tile of KPT keys: NLD loads per operand, each covering KPL keys.
+// A tile holds the same bytes at either head dim (64 keys of 64, 32 keys of 128).
+template <typename T, int HD>
 struct Tile {
   static constexpr int EPL = KvTraits<T>::kElemsPerLoad;  // elements per lane per load
-  static constexpr int LPK = kAttnHeadDim / EPL;          // lanes per key row: 8 (bf16), 16 (f32)
+  static constexpr int LPK = HD / EPL;                    // lanes per key row: 8 / 16 (bf16),
+                                                          // 16 / 32 (f32) at HD 64 / 128
   static constexpr int KPL = kWave / LPK;                 // keys per wave-wide load
-  static constexpr int NLD = kAttnKeysPerTile / KPL;      // loads per operand per tile
+  static constexpr int KPT = attn_keys_per_tile(HD);      // keys per tile
+  static constexpr int NLD = KPT / KPL;                   // loads per operand per tile
   u32x4 k[NLD], v[NLD];
 
   // Buffer loads through a descriptor that spans exactly the sequence's valid
@@ -203,7 +209,7 @@ struct Tile {
   // consume).  lane_off is this lane's byte offset inside a wave-wide load.
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                        int base, int lane_off) {
-    constexpr int kRowBytes = kAttnHeadDim * (int)sizeof(T);
+    constexpr int kRowBytes = HD * (int)sizeof(T);
     const int tile_off = base * kRowBytes + lane_off;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -272,16 +278,19 @@ __device__ __forceinline__ void store_out(const AttnSeg& S, size_t i, float a, f
 }
 
 // PAGED: segments with a block table read each tile through a descriptor over its block of
-// the pool (a 64-key tile never crosses a block); other segments read the static layout.
-// EX: the widened entry point -- segments with a key bitmask skip the keys whose bit
-// is clear, and outputs may be bf16.
-template <typename T, bool PAGED, bool EX = false>
+// the pool (a tile of at most 64 keys never crosses a block); other segments read the
+// static layout.  EX: the widened entry point -- segments with a key bitmask skip the
+// keys whose bit is clear, and outputs may be bf16.  HD: head dim, 64 or 128.
+template <typename T, bool PAGED, bool EX, int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p) {
-  constexpr int HD = kAttnHeadDim;
-  using TileT = Tile<T>;
+  using TileT = Tile<T, HD>;
   constexpr int EPL = TileT::EPL;
   constexpr int LPK = TileT::LPK;
-  constexpr int TPC = kAttnTilesPerChunk;
+  constexpr int KPT = TileT::KPT;
+  constexpr int TPC = attn_tiles_per_chunk(HD);
+  constexpr int PS = attn_part_stride(HD);
+  static_assert(kAttnThreads % HD == 0, "whole sequences per combining pass");
+  static_assert(!EX || KPT == 32 || KPT == 64, "a tile's mask bits are one or two whole words");
 
   extern __shared__ int s_dyn[];  // [G] lengths, [G] order, [G+1] item prefix
   __shared__ float s_acc[kAttnWaves][HD];
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
       n = len[cross ? lane - B : lane];
       n = n < 0 ? 0 : (n > cap ? cap : n);
-      items = group_items(n, NLH, cpi);
+      items = group_items<HD>(n, NLH, cpi);
     }
     int rank = 0;  // stable rank by descending length
     for (int j = 0; j < G; ++j) {
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const int lo = min(G, tid * per);
     const int hi = min(G, lo + per);
     int local = 0;
-    for (int i = lo; i < hi; ++i) local += group_items(s_n[s_order[i]], NLH, cpi);
+    for (int i = lo; i < hi; ++i) local += group_items<HD>(s_n[s_order[i]], NLH, cpi);
     int ex = wave_inclusive_sum_int(local, lane) - local;
     if (lane == kWave - 1) s_wsum[wave] = ex + local;
     __syncthreads();
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     }
     for (int i = lo; i < hi; ++i) {
       s_pref[i] = ex;
-      ex += group_items(s_n[s_order[i]], NLH, cpi);
+      ex += group_items<HD>(s_n[s_order[i]], NLH, cpi);
     }
     if (tid == 0) s_pref[G] = total;
     __syncthreads();
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const AttnSeg& S = cross ? p.seg[1] : p.seg[0];
     const int b = cross ? g - B : g;
     const int nck = nchunks(n);
-    const int spw = waves_per_seq(n);            // waves per sequence
+    const int spw = waves_per_seq<HD>(n);        // waves per sequence
     const bool packed = spw < kAttnWaves;        // several sequences share this item
     const int P = kAttnWaves / spw;              // sequences in this item (packed)
 
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       continue;
     }
 
-    constexpr int kStep = kAttnWaves * kAttnKeysPerTile;  // keys between a wave's tiles
+    constexpr int kStep = kAttnWaves * KPT;  // keys between a wave's tiles
     constexpr int kRowBytes = HD * (int)sizeof(T);
     const int lane_off = kg * kRowBytes + dl * 16;
     const bool paged = PAGED && S.table != nullptr;  // uniform: per segment
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
 
     for (int c = c0; c < c1; ++c) {
       // tile t of this wave starts at key cb + t * kStep; packed items read one tile
-      const int cb = c * kAttnChunk + wave_part * kAttnKeysPerTile;
+      const int cb = c * kAttnChunk + wave_part * KPT;
       float m_g = -INFINITY, l_g = 0.f;  // this lane group's online state
       float acc[EPL];
 #pragma unroll
@@ -479,9 +488,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           // pipeline's last prefetch moves no bytes (the next chunk loads its own)
           if (t >= nt) return {rk_none, rv_none, 0, 0ull};
           uint64_t keep = ~0ull;
-          if (EX && S.mask != nullptr)  // the tile's 64 mask bits (two words, uniform)
-            keep = *reinterpret_cast<const uint64_t*>(S.mask + (size_t)b * S.mask_words +
-                                                      (base >> 5));
+          if (EX && S.mask != nullptr) {  // the tile's KPT mask bits (uniform)
+            const uint32_t* mw = S.mask + (size_t)b * S.mask_words + (base >> 5);
+            keep = KPT == 64 ? *reinterpret_cast<const uint64_t*>(mw) : (uint64_t)*mw;
+          }
           if (!paged) return {rk_seq, rv_seq, base, keep};
           const int bs = 1 << S.bs_log2;
           const int row = base & (bs - 1);
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
         if (whole) {
           fold_chunk<EX>(c == c0, mc, lc, ac, fm, fl, fa);
         } else {  // publish the chunk state, write-through
-          float* pp = S.part + (slot_sidx * S.nck_cap + c) * kAttnPartStride;
+          float* pp = S.part + (slot_sidx * S.nck_cap + c) * PS;
           __hip_atomic_store(pp + 4 + d, ac, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (d == 0) {
             __hip_atomic_store(pp, mc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -569,9 +579,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     __syncthreads();
     if (s_last) {
       if (slot_ok) {
-        const float* pp = S.part + slot_sidx * S.nck_cap * kAttnPartStride;
+        const float* pp = S.part + slot_sidx * S.nck_cap * PS;
         for (int cc = 0; cc < nck; ++cc) {
-          const float* q = pp + cc * kAttnPartStride;
+          const float* q = pp + cc * PS;
           const float mc = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const float lc = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const float ac = __hip_atomic_load(q + 4 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -599,21 +609,31 @@ long long attn_items_cap(const AttnParams& p) {
 namespace {
 struct DevInfo {
   int cus = 0;
-  int occ[2][3] = {{0, 0, 0}, {0, 0, 0}};  // resident workgroups per CU [dtype][variant]
+  int occ[2][2][3] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
 };
 DevInfo g_dev[64];
+
+// variant: 0 static, 1 paged, 2 widened (key masks / bf16 outputs, static caches)
+template <typename T, int HD>
+void* attn_kernel_ptr(int variant) {
+  return variant == 2   ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, true, HD>)
+         : variant == 1 ? reinterpret_cast<void*>(&attn_decode_kernel<T, true, false, HD>)
+                        : reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD>);
+}
+
+template <typename T, int HD>
+void attn_kernel_go(int variant, int blocks, size_t lds, hipStream_t stream, const AttnParams& p) {
+  if (variant == 2)
+    hipLaunchKernelGGL((attn_decode_kernel<T, false, true, HD>), dim3(blocks), dim3(kAttnThreads),
+                       lds, stream, p);
+  else if (variant == 1)
+    hipLaunchKernelGGL((attn_decode_kernel<T, true, false, HD>), dim3(blocks), dim3(kAttnThreads),
+                       lds, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_kernel<T, false, false, HD>), dim3(blocks), dim3(kAttnThreads),
+                       lds, stream, p);
+}
 }  // namespace
-
-template <typename T, bool PAGED, bool EX>
-static void* attn_kernel_ptr() {
-  return reinterpret_cast<void*>(&attn_decode_kernel<T, PAGED, EX>);
-}
-
-template <typename T, bool PAGED, bool EX>
-static void attn_kernel_go(int blocks, size_t lds, hipStream_t stream, const AttnParams& p) {
-  hipLaunchKernelGGL((attn_decode_kernel<T, PAGED, EX>), dim3(blocks), dim3(kAttnThreads), lds,
-                     stream, p);
-}
 
 hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream) {
   const int G = p.nseg * p.B;
@@ -621,15 +641,13 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
   const bool paged = p.seg[0].table != nullptr || (p.nseg > 1 && p.seg[1].table != nullptr);
   const bool ex = p.seg[0].mask != nullptr || p.seg[0].out_bf16 ||
                   (p.nseg > 1 && (p.seg[1].mask != nullptr || p.seg[1].out_bf16));
-  // instantiations: static, paged, widened (key masks / bf16 outputs, static caches)
   const int variant = ex ? 2 : paged ? 1 : 0;
-  void* fn = dtype == 0
-                 ? (variant == 2 ? attn_kernel_ptr<uint16_t, false, true>()
-                    : variant == 1 ? attn_kernel_ptr<uint16_t, true, false>()
-                                   : attn_kernel_ptr<uint16_t, false, false>())
-                 : (variant == 2 ? attn_kernel_ptr<float, false, true>()
-                    : variant == 1 ? attn_kernel_ptr<float, true, false>()
-                                   : attn_kernel_ptr<float, false, false>());
+  const int wide = p.hd == kAttnHeadDimWide ? 1 : 0;
+  if (!wide && p.hd != kAttnHeadDim) return hipErrorInvalidValue;
+  void* fn = dtype == 0 ? (wide ? attn_kernel_ptr<uint16_t, kAttnHeadDimWide>(variant)
+                                : attn_kernel_ptr<uint16_t, kAttnHeadDim>(variant))
+                        : (wide ? attn_kernel_ptr<float, kAttnHeadDimWide>(variant)
+                                : attn_kernel_ptr<float, kAttnHeadDim>(variant));
   if (blocks <= 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -641,12 +659,12 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
       if (e != hipSuccess) return e;
       di.cus = cus;
     }
-    int occ = di.occ[dtype][variant];
+    int occ = di.occ[dtype][wide][variant];
     if (occ == 0 || G > 64) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);
       if (e != hipSuccess) return e;
       if (occ < 1) occ = 1;
-      if (G <= 64) di.occ[dtype][variant] = occ;
+      if (G <= 64) di.occ[dtype][wide][variant] = occ;
     }
     const long long cap = attn_items_cap(p);
     const long long want = (long long)di.cus * occ;
@@ -654,13 +672,11 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
   }
   if (blocks < 1) blocks = 1;
   if (dtype == 0) {
-    if (variant == 2) attn_kernel_go<uint16_t, false, true>(blocks, lds, stream, p);
-    else if (variant == 1) attn_kernel_go<uint16_t, true, false>(blocks, lds, stream, p);
-    else attn_kernel_go<uint16_t, false, false>(blocks, lds, stream, p);
+    if (wide) attn_kernel_go<uint16_t, kAttnHeadDimWide>(variant, blocks, lds, stream, p);
+    else attn_kernel_go<uint16_t, kAttnHeadDim>(variant, blocks, lds, stream, p);
   } else {
-    if (variant == 2) attn_kernel_go<float, false, true>(blocks, lds, stream, p);
-    else if (variant == 1) attn_kernel_go<float, true, false>(blocks, lds, stream, p);
-    else attn_kernel_go<float, false, false>(blocks, lds, stream, p);
+    if (wide) attn_kernel_go<float, kAttnHeadDimWide>(variant, blocks, lds, stream, p);
+    else attn_kernel_go<float, kAttnHeadDim>(variant, blocks, lds, stream, p);
   }
   return hipGetLastError();
 }

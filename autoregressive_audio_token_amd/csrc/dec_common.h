@@ -23,14 +23,15 @@ __device__ __forceinline__ float dpp_f32(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of G lanes (G = 8 or 16); every lane of a group gets the sum.
+// Sum over aligned groups of G lanes (G = 8, 16 or 32); every lane of a group gets the sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+  static_assert(G == 8 || G == 16 || G == 32, "group of 8, 16 or 32 lanes");
   v += dpp_f32<kDppQuadXor1>(v);
   v += dpp_f32<kDppQuadXor2>(v);
   v += dpp_f32<kDppHalfMirror>(v);
-  if constexpr (G == 16) v += dpp_f32<kDppRowMirror>(v);
+  if constexpr (G >= 16) v += dpp_f32<kDppRowMirror>(v);
+  if constexpr (G == 32) v += __shfl_xor(v, 16);
   return v;
 }
 

@@ -17,16 +17,24 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 #ifndef DEC_ATTN_TILE_KEYS
 #define DEC_ATTN_TILE_KEYS 64
 #endif
-constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile
+constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile at head
+                                                    // dim 64 (at 128: half, same bytes)
 #ifndef DEC_ATTN_CHUNK
 #define DEC_ATTN_CHUNK 1024
 #endif
 constexpr int kAttnChunk = DEC_ATTN_CHUNK;          // keys per chunk
-constexpr int kAttnTilesPerChunk = kAttnChunk / (kAttnWaves * kAttnKeysPerTile);
-static_assert(kAttnTilesPerChunk * kAttnWaves * kAttnKeysPerTile == kAttnChunk,
+constexpr int kAttnHeadDim = 64;                   // the model's head dim; 128 is also built
+constexpr int kAttnHeadDimWide = 128;
+// keys per tile and tiles per chunk at head dim HD
+constexpr int attn_keys_per_tile(int hd) { return kAttnKeysPerTile * kAttnHeadDim / hd; }
+constexpr int attn_tiles_per_chunk(int hd) { return kAttnChunk / (kAttnWaves * attn_keys_per_tile(hd)); }
+static_assert(attn_tiles_per_chunk(kAttnHeadDim) * kAttnWaves * kAttnKeysPerTile == kAttnChunk,
               "a chunk is a whole number of workgroup tile rounds");
-constexpr int kAttnPartStride = 68;                 // floats per chunk partial: m, l, pad, pad, acc[64]
-constexpr int kAttnHeadDim = 64;
+static_assert(attn_tiles_per_chunk(kAttnHeadDimWide) * kAttnWaves *
+                      attn_keys_per_tile(kAttnHeadDimWide) == kAttnChunk,
+              "a chunk is a whole number of workgroup tile rounds");
+// floats per chunk partial: m, l, pad, pad, acc[hd]
+constexpr int attn_part_stride(int hd) { return 4 + hd; }
 constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
 constexpr int kAttnSortMax = 1024;                  // groups ordered longest-first up to this count
 constexpr int kAttnSplitBelow = 512;                // below this many sequences per launch, every
@@ -34,16 +42,16 @@ constexpr int kAttnSplitBelow = 512;                // below this many sequences
 
 // One attention problem ("segment"): self-attention or cross-attention of a step.
 struct AttnSeg {
-  const void* q;          // [NL, B, H, 64]
-  const void* k;          // [NL, B, H, L_cap, 64]
-  const void* v;          // [NL, B, H, L_cap, 64]
+  const void* q;          // [NL, B, H, hd]
+  const void* k;          // [NL, B, H, L_cap, hd]
+  const void* v;          // [NL, B, H, L_cap, hd]
   const int32_t* len;     // [B] valid slots
-  void* out;              // [NL, B, H, 64] fp32, or bf16 when out_bf16
-  float* part;            // [NL*B*H, nck_cap, kAttnPartStride] chunk partials (split mode)
+  void* out;              // [NL, B, H, hd] fp32, or bf16 when out_bf16
+  float* part;            // [NL*B*H, nck_cap, attn_part_stride(hd)] chunk partials (split mode)
   int32_t* ticket;        // [NL*B*H] chunk arrival counters (split mode), zero between calls
   int L_cap;              // keys a sequence can hold (paged: table_stride << bs_log2)
   int nck_cap;            // ceil(L_cap / kAttnChunk)
-  // paged cache (table != nullptr): k, v are pools [NL, n_blocks, H, 1 << bs_log2, 64]
+  // paged cache (table != nullptr): k, v are pools [NL, n_blocks, H, 1 << bs_log2, hd]
   const int32_t* table;   // [B, table_stride] physical block of each logical block
   int table_stride;
   int n_blocks;           // physical blocks per layer
@@ -58,6 +66,7 @@ struct AttnParams {
   AttnSeg seg[2];
   int nseg;
   int NL, B, H;
+  int hd;                 // 64 or 128 (selects the instantiation)
   int cpi;                // chunks per work item (>= nck_cap of every segment: no split)
   float qscale;           // scale * log2(e): scores are formed in base 2
 };

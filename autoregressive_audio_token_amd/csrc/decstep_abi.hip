@@ -29,7 +29,7 @@ struct SegLayout {
   int nck_cap = 0;
 };
 
-SegLayout seg_layout(int NL, int B, int H, int L_cap) {
+SegLayout seg_layout(int NL, int B, int H, int L_cap, int hd) {
   SegLayout s;
   if (L_cap <= 0) return s;
   s.nck_cap = (L_cap + dec::kAttnChunk - 1) / dec::kAttnChunk;
@@ -37,15 +37,17 @@ SegLayout seg_layout(int NL, int B, int H, int L_cap) {
   const size_t nseq = (size_t)NL * B * H;
   s.ticket_off = 0;
   s.part_off = align_up(nseq * sizeof(int32_t), 256);
-  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::kAttnPartStride * sizeof(float), 256);
+  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::attn_part_stride(hd) * sizeof(float), 256);
   return s;
 }
 
-bool sizes_ok(int NL, int B, int H, int L_cap) {
+bool hd_ok(int hd) { return hd == dec::kAttnHeadDim || hd == dec::kAttnHeadDimWide; }
+
+bool sizes_ok(int NL, int B, int H, int L_cap, int hd) {
   if (NL < 1 || B < 1 || H < 1 || L_cap < 1) return false;
   const long long nseq = (long long)NL * B * H;
   if (nseq > (1LL << 30)) return false;
-  const long long elems = nseq * L_cap * dec::kAttnHeadDim;
+  const long long elems = nseq * L_cap * hd;
   return elems < (1LL << 46);
 }
 
@@ -82,7 +84,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   }
   if (dtype != DEC_BF16 && dtype != DEC_F32) return DEC_E_DTYPE;
   for (int s = 0; s < nseg; ++s) {
-    if (!sizes_ok(NL, B, H, segs[s].L_cap)) return DEC_E_SHAPE;
+    if (!sizes_ok(NL, B, H, segs[s].L_cap, hd > 0 ? hd : 1)) return DEC_E_SHAPE;
   }
   for (int s = 0; s < nseg; ++s) {
     const SegArgs& a = segs[s];
@@ -96,8 +98,12 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
       return DEC_E_UNSUPPORTED;
     if (!aligned(a.table, 4)) return DEC_E_ALIGN;
   }
-  if (hd != dec::kAttnHeadDim) return DEC_E_UNSUPPORTED;
+  if (!hd_ok(hd)) return DEC_E_UNSUPPORTED;
   if (nseg * B > dec::kAttnMaxGroups) return DEC_E_UNSUPPORTED;
+  for (int s = 0; s < nseg; ++s) {  // one sequence's static cache: 32-bit byte offsets
+    const long long seq_bytes = (long long)segs[s].L_cap * hd * (dtype == DEC_BF16 ? 2 : 4);
+    if (segs[s].table == nullptr && seq_bytes > 0x7FFFFFFFLL) return DEC_E_UNSUPPORTED;
+  }
   for (int s = 0; s < nseg; ++s) {
     if (!aligned(segs[s].q, 16) || !aligned(segs[s].k, 16) || !aligned(segs[s].v, 16) ||
         !aligned(segs[s].len, 4) || !aligned(segs[s].out, segs[s].out_bf16 ? 2 : 4))
@@ -113,7 +119,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   size_t need = 0;
   SegLayout lay[2];
   for (int s = 0; s < nseg; ++s) {
-    lay[s] = seg_layout(NL, B, H, segs[s].L_cap);
+    lay[s] = seg_layout(NL, B, H, segs[s].L_cap, hd);
     need += lay[s].bytes;
   }
   if (need > 0) {
@@ -127,6 +133,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   p.NL = NL;
   p.B = B;
   p.H = H;
+  p.hd = hd;
   p.qscale = scale * 1.4426950408889634f;  // log2(e)
   int nck_max = 1;
   size_t off = 0;
@@ -172,11 +179,10 @@ int dec_attn_chunk_keys(void) { return dec::kAttnChunk; }
 
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_self,
                                 int L_cap_cross) {
-  if (hd != dec::kAttnHeadDim || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 0 ||
-      L_cap_cross < 0)
+  if (!hd_ok(hd) || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 0 || L_cap_cross < 0)
     return 0;
-  return seg_layout(n_layers, B, H, L_cap_self).bytes +
-         seg_layout(n_layers, B, H, L_cap_cross).bytes;
+  return seg_layout(n_layers, B, H, L_cap_self, hd).bytes +
+         seg_layout(n_layers, B, H, L_cap_cross, hd).bytes;
 }
 
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {

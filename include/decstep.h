@@ -50,7 +50,7 @@ enum dec_status {
   DEC_E_SHAPE = 2,        /* a size is out of range or sizes disagree */
   DEC_E_DTYPE = 3,        /* unknown dtype code */
   DEC_E_WORKSPACE = 4,    /* workspace smaller than dec_attn_workspace_bytes() */
-  DEC_E_UNSUPPORTED = 5,  /* a legal but unimplemented case (e.g. head_dim != 64) */
+  DEC_E_UNSUPPORTED = 5,  /* a legal but unimplemented case (e.g. head_dim other than 64 or 128) */
   DEC_E_HIP = 6,          /* a HIP runtime call failed */
   DEC_E_ALIGN = 7         /* a pointer is not aligned as required */
 };
@@ -88,7 +88,9 @@ int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t strea
  *   len  [B] int32, valid slots of sequence b INCLUDING the current token
  *   out  [n_layers, B, H, hd] float32:
  *          out = sum_j softmax_j(scale * <q, k_j>) v_j   over j < len[b]
- *   hd must be 64; dtype is DEC_BF16 or DEC_F32; accumulation is float32.
+ *   hd is 64 (the model's head size) or 128; dtype is DEC_BF16 or DEC_F32;
+ *   accumulation is float32.  One sequence's cache, L_cap * hd * element
+ *   size, must stay below 2 GiB (else DEC_E_UNSUPPORTED).
  * Device-side values: len[b] <= 0 gives an all-zero output row; len[b] >
  * L_cap is read as L_cap.  n_layers > 1 means layer-stacked buffers served by
  * one launch.  B is at most 4096 (2048 for dec_attn_step): DEC_E_UNSUPPORTED. */
@@ -123,8 +125,9 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
  *               hidden by an attention mask).  Bit j % 32 of word j / 32 of row b
  *               set = key j attended.  Keys j < enc_len[b] with their bit set
  *               take part; a row with none outputs zeros.  mask_words must be
- *               even and at least 2 * ceil(L_cap_cross / 64) (each 64-key tile
- *               reads two whole words); 8-byte aligned.
+ *               even and at least 2 * ceil(L_cap_cross / 64) (a tile reads whole
+ *               words: two per 64 keys at hd 64, one per 32 keys at hd 128);
+ *               8-byte aligned.
  *   out_dtype   DEC_F32 (float outputs, as dec_attn_step) or DEC_BF16 (outputs
  *               rounded to bfloat16, nearest-even, from the same fp32 values;
  *               out pointers 2-byte aligned).
@@ -151,7 +154,8 @@ int dec_attn_step_ex(const void* q_self, const void* k_self, const void* v_self,
  *                table for every layer and head)
  *   len          [B] int32, clamped to [0, max_blocks * block_size]
  *   out          [n_layers, B, H, hd] float32
- * block_size: a power of two, at least 64 (a 64-key tile never crosses a block),
+ * block_size: a power of two, at least 64 (a tile, 64 keys at hd 64 and 32 at
+ * hd 128, never crosses a block),
  * else DEC_E_UNSUPPORTED.  Workspace: dec_attn_workspace_bytes with
  * L_cap_self = max_blocks * block_size.  Device-side: a table entry outside
  * [0, n_blocks) makes that block read as zero rows (nothing outside the pool is

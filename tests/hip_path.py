@@ -14,14 +14,15 @@ def code(w):
 
 def workspace(w, self_cap, cross_cap, batch=None):
     B = w.batch if batch is None else batch
-    nbytes = dec.dec_attn_workspace_bytes(w.n_layers, B, w.heads, HD, self_cap, cross_cap)
+    nbytes = dec.dec_attn_workspace_bytes(w.n_layers, B, w.heads, w.head_dim, self_cap, cross_cap)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
     dec.dec_attn_workspace_init(ws, nbytes)
     return ws, nbytes
 
 
 def out_buf(w, fill=float("nan")):
-    return torch.full((w.n_layers, w.batch, w.heads, HD), fill, dtype=torch.float32, device=DEV)
+    return torch.full((w.n_layers, w.batch, w.heads, w.head_dim), fill, dtype=torch.float32,
+                      device=DEV)
 
 
 def attn(kind, w, d, ws=None, lens=None, scale=None, cap=None, k=None, v=None):
@@ -34,7 +35,7 @@ def attn(kind, w, d, ws=None, lens=None, scale=None, cap=None, k=None, v=None):
     v = d[f"v_{kind}"] if v is None else v
     out = out_buf(w)
     fn = dec.dec_attn_self if kind == "self" else dec.dec_attn_cross
-    fn(d[f"q_{kind}"], k, v, lens, out, w.n_layers, w.batch, w.heads, cap, HD, code(w),
+    fn(d[f"q_{kind}"], k, v, lens, out, w.n_layers, w.batch, w.heads, cap, w.head_dim, code(w),
        w.scale if scale is None else scale, ws[0], ws[1])
     return out
 
@@ -45,7 +46,7 @@ def attn_step(w, d, ws=None, scale=None):
     o_s, o_c = out_buf(w), out_buf(w)
     dec.dec_attn_step(d["q_self"], d["k_self"], d["v_self"], d["len"], w.self_cap, o_s,
                       d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"], w.cross_cap, o_c,
-                      w.n_layers, w.batch, w.heads, HD, code(w),
+                      w.n_layers, w.batch, w.heads, w.head_dim, code(w),
                       w.scale if scale is None else scale, ws[0], ws[1])
     return o_s, o_c
 
@@ -71,10 +72,12 @@ def host(t):
 
 
 def row_rel_err(got, want):
-    """max over rows of ||got - want||_inf / ||want||_inf (rows with want == 0 compare
-    absolutely)."""
-    got = np.asarray(got, np.float64).reshape(-1, HD)
-    want = np.asarray(want, np.float64).reshape(-1, HD)
+    """max over rows (the last axis) of ||got - want||_inf / ||want||_inf (rows with
+    want == 0 compare absolutely)."""
+    want = np.asarray(want, np.float64)
+    hd = want.shape[-1]
+    got = np.asarray(got, np.float64).reshape(-1, hd)
+    want = want.reshape(-1, hd)
     num = np.max(np.abs(got - want), axis=1)
     den = np.max(np.abs(want), axis=1)
     den = np.where(den == 0, 1.0, den)

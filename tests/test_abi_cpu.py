@@ -78,8 +78,10 @@ def test_attention_host_validation():
     assert _attn(dt=2) == D.DEC_E_DTYPE
     for bad in (dict(NL=0), dict(B=0), dict(H=-1), dict(L=0), dict(B=1 << 20, H=1 << 11)):
         assert _attn(**bad) == D.DEC_E_SHAPE, bad
-    assert _attn(hd=128) == D.DEC_E_UNSUPPORTED
+    for hd in (32, 96, 256):                     # head dims 64 and 128 are built
+        assert _attn(hd=hd) == D.DEC_E_UNSUPPORTED, hd
     assert _attn(B=5000) == D.DEC_E_UNSUPPORTED
+    assert _attn(L=1 << 22, hd=128, dt=1) == D.DEC_E_UNSUPPORTED   # 2 GiB per sequence
     assert _attn(q=A + 8) == D.DEC_E_ALIGN
     assert _attn(out=A + 2) == D.DEC_E_ALIGN
     # a cache longer than one chunk needs the workspace
@@ -108,6 +110,9 @@ def test_step_validation_and_workspace_sizes():
     assert dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 3 * ck) == s + c
     assert s >= 24 * 10 * 68 * 4 and c >= 24 * 3 * 68 * 4
     assert dec.dec_attn_workspace_bytes(2, 3, 4, 32, 10, 10) == 0
+    # head dim 128: chunk states of 4 + 128 floats
+    w128 = dec.dec_attn_workspace_bytes(2, 3, 4, 128, 10 * ck, 0)
+    assert w128 >= 24 * 10 * 132 * 4 and w128 > s
 
 
 def _samp(**kw):
@@ -148,7 +153,7 @@ def test_paged_attention_host_validation():
     for bad in (dict(nb=0), dict(mb=0), dict(bs=0), dict(NL=0), dict(B=0),
                 dict(mb=1 << 20, bs=1 << 12), dict(nb=1 << 30)):
         assert _paged(**bad) == D.DEC_E_SHAPE, bad
-    for bad in (dict(bs=32), dict(bs=96), dict(bs=1 << 21), dict(hd=128)):
+    for bad in (dict(bs=32), dict(bs=96), dict(bs=1 << 21), dict(hd=96)):
         assert _paged(**bad) == D.DEC_E_UNSUPPORTED, bad
     assert _paged(tab=A + 2) == D.DEC_E_ALIGN
     assert _paged(k=A + 8) == D.DEC_E_ALIGN
