@@ -491,6 +491,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           if (EX && S.mask != nullptr) {  // the tile's KPT mask bits (uniform)
             const uint32_t* mw = S.mask + (size_t)b * S.mask_words + (base >> 5);
             keep = KPT == 64 ? *reinterpret_cast<const uint64_t*>(mw) : (uint64_t)*mw;
+            // no attended key in the tile: nothing to read (every score is masked)
+            if (keep == 0ull) return {rk_none, rv_none, 0, 0ull};
           }
           if (!paged) return {rk_seq, rv_seq, base, keep};
           const int bs = 1 << S.bs_log2;

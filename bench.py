@@ -13,6 +13,7 @@ Prints ONE JSON line: value = valid K/V bytes per step / time per step (GB/s).
     python bench.py [--steps K] [--warmup W] [--workload long_description]
 """
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -47,6 +48,19 @@ def parse(argv=None):
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB five times and exit;\n"
                          "the calibration for the HBM byte counters")
+    ap.add_argument("--head-dim", type=int, default=64, choices=(64, 128),
+                    help="128: the same model width as heads of 128 (half the heads)")
+    ap.add_argument("--cross-mask", type=float, default=0.0, metavar="P",
+                    help="a boolean description mask keeping each key with probability P\n"
+                         "(seeded), through the widened entry dec_attn_step_ex")
+    ap.add_argument("--mask-runs", type=int, default=0, metavar="R",
+                    help="with --cross-mask: masked keys come in runs of R keys (0: single keys)")
+    ap.add_argument("--out-bf16", action="store_true",
+                    help="bf16 attention outputs, through dec_attn_step_ex")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="sampler top_k (0: the workload's); above 64 through dec_sample_topk_ex")
+    ap.add_argument("--logits-bf16", action="store_true",
+                    help="bf16 logits, through dec_sample_topk_ex")
     return ap.parse_args(argv)
 
 
@@ -242,10 +256,40 @@ def main(argv=None):
     w = configs.BY_NAME[a.workload]
     if a.heads:
         return heads_bench(a, w)
+    if a.head_dim != w.head_dim:     # the same model width in heads of a.head_dim
+        w = dataclasses.replace(w, heads=w.heads * w.head_dim // a.head_dim, head_dim=a.head_dim,
+                                scale=a.head_dim ** -0.5, qkv_std=a.head_dim ** -0.5)
+    top_k = a.top_k if a.top_k > 0 else w.top_k
+    ex_attn = a.cross_mask > 0 or a.out_bf16
+    ex_samp = top_k > 64 or a.logits_bf16
+    if ex_attn and a.paged:
+        print("--cross-mask / --out-bf16 go with the static caches, not --paged", file=sys.stderr)
+        return 2
+    plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s_len, c_len = gen.lengths(w)
     valid = configs.valid_kv_bytes(w, s_len, c_len)
+    mask_d, mask_words, mask_note = None, 0, None
+    if a.cross_mask > 0:
+        # seeded boolean description mask; algorithmic bytes count attended keys only
+        rng = np.random.default_rng(777)
+        if a.mask_runs > 0:
+            runs = rng.random((w.batch, -(-w.cross_cap // a.mask_runs))) < a.cross_mask
+            mask = np.repeat(runs, a.mask_runs, axis=1)[:, :w.cross_cap]
+        else:
+            mask = rng.random((w.batch, w.cross_cap)) < a.cross_mask
+        mask_words = 2 * ((w.cross_cap + 63) // 64)
+        padded = np.zeros((w.batch, mask_words * 32), bool)
+        padded[:, :w.cross_cap] = mask
+        packed = np.ascontiguousarray(np.packbits(padded, axis=1, bitorder="little")).view(np.uint32)
+        mask_d = torch.from_numpy(packed.copy()).to(dev)
+        attended = sum(int(mask[b, :int(c_len[b])].sum()) for b in range(w.batch))
+        row = w.head_dim * (2 if w.dtype == "bf16" else 4)
+        cross_all = sum(int(n) for n in c_len) * w.n_layers * w.heads * row * 2
+        valid = valid - cross_all + attended * w.n_layers * w.heads * row * 2
+        mask_note = (f"keep probability {a.cross_mask}, runs of {a.mask_runs or 1} keys: "
+                     f"{attended} of {int(sum(c_len))} description keys attended")
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
     log(f"workload {w.name}: staging inputs")
     d = wdev.step_inputs(w, dev)
@@ -259,9 +303,10 @@ def main(argv=None):
     nb = dec.dec_attn_workspace_bytes(w.n_layers, w.batch, w.heads, w.head_dim, w.self_cap,
                                       w.cross_cap)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-    o_s = torch.empty((w.n_layers, w.batch, w.heads, w.head_dim), dtype=torch.float32,
-                      device=dev)
+    o_s = torch.empty((w.n_layers, w.batch, w.heads, w.head_dim),
+                      dtype=torch.bfloat16 if a.out_bf16 else torch.float32, device=dev)
     o_c = torch.empty_like(o_s)
+    logits = d["logits"].to(torch.bfloat16) if a.logits_bf16 else d["logits"]
     tok = torch.empty((w.batch, w.n_codebooks), dtype=torch.int32, device=dev)
     step_t = d["step"] if w.delay else None
     stream = torch.cuda.Stream(device=dev)
@@ -289,6 +334,13 @@ def main(argv=None):
         torch.cuda.synchronize()
 
     def attn(st, s):
+        if ex_attn:
+            dec.dec_attn_step_ex(d["q_self"], st["k_self"], st["v_self"], d["len"], w.self_cap,
+                                 o_s, d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"],
+                                 mask_d, mask_words, w.cross_cap, o_c, w.n_layers, w.batch,
+                                 w.heads, w.head_dim, code,
+                                 dec.DEC_BF16 if a.out_bf16 else dec.DEC_F32, w.scale, ws, nb, s)
+            return
         if a.paged:
             dec.dec_attn_step_paged(d["q_self"], st["k_self"], st["v_self"], table, d["len"],
                                     a.paged, n_blocks, w.self_cap // a.paged, o_s, d["q_cross"],
@@ -302,8 +354,14 @@ def main(argv=None):
                           s)
 
     def sample(s):
-        dec.dec_sample_topk(d["logits"], w.batch, w.n_codebooks, w.vocab_valid, w.vocab_stride,
-                            d["temperature"], w.top_k, d["uniforms"], step_t, w.fill_token, tok,
+        if ex_samp:
+            dec.dec_sample_topk_ex(logits, dec.DEC_BF16 if a.logits_bf16 else dec.DEC_F32,
+                                   w.batch, w.n_codebooks, w.vocab_valid, w.vocab_stride,
+                                   d["temperature"], top_k, d["uniforms"], 0, step_t,
+                                   w.fill_token, tok, None, None, s)
+            return
+        dec.dec_sample_topk(logits, w.batch, w.n_codebooks, w.vocab_valid, w.vocab_stride,
+                            d["temperature"], top_k, d["uniforms"], step_t, w.fill_token, tok,
                             None, None, s)
 
     torch.cuda.synchronize()
@@ -387,9 +445,27 @@ def main(argv=None):
     pair_us = sum(per) / len(per)
     achieved = valid / (k_us * 1e-6) / 1e9
     dec.dec_graph_destroy(graph)
+    # the sampler alone: a captured graph of n_k launches
+    with torch.cuda.stream(stream):
+        dec.dec_graph_begin(stream)
+        for _ in range(n_k):
+            sample(stream)
+        sgraph = dec.dec_graph_end(stream)
+        dec.dec_graph_launch(sgraph, stream)        # warm
+    stream.synchronize()
+    k0.record(stream)
+    for _ in range(k_reps):
+        dec.dec_graph_launch(sgraph, stream)
+    k1.record(stream)
+    stream.synchronize()
+    samp_us = k0.elapsed_time(k1) * 1e3 / (k_reps * n_k)
+    dec.dec_graph_destroy(sgraph)
     traffic_rec, traffic_why = counter_traffic(w.name)
-    if a.paged:
-        traffic_rec, traffic_why = None, "counters describe the static layout"
+    if not plain:
+        traffic_rec, traffic_why = None, "counters describe the default configuration only"
+    attn_entry = ("dec_attn_step_ex" if ex_attn else
+                  "dec_attn_step_paged" if a.paged else "dec_attn_step")
+    samp_entry = "dec_sample_topk_ex" if ex_samp else "dec_sample_topk"
 
     result = {
         "metric": METRIC,
@@ -410,19 +486,20 @@ def main(argv=None):
             "head_dim": w.head_dim, "self_len": [int(x) for x in s_len][:4],
             "self_cap": w.self_cap, "cross_len": [int(x) for x in c_len][:4],
             "cross_cap": w.cross_cap, "codebooks": w.n_codebooks, "vocab": w.vocab_valid,
-            "vocab_stride": w.vocab_stride, "top_k": w.top_k, "accumulate": "f32",
+            "vocab_stride": w.vocab_stride, "top_k": top_k, "accumulate": "f32",
             "valid_kv_bytes_per_step": valid, "cache_sets": R,
             "static_cache_bytes_per_set": static_bytes,
             "kv_layout": (f"self cache paged, {a.paged} keys per block" if a.paged
                           else "static caches"),
-            "schedule": f"hipGraph of R steps; step = "
-                        f"{'dec_attn_step_paged' if a.paged else 'dec_attn_step'} (self+cross, "
-                        f"all layers, one launch) + dec_sample_topk",
+            "schedule": f"hipGraph of R steps; step = {attn_entry} (self+cross, all layers, "
+                        f"one launch) + {samp_entry}",
+            "variant": {"head_dim": w.head_dim, "cross_mask": mask_note,
+                        "attention_outputs": "bf16" if a.out_bf16 else "f32",
+                        "logits": "bf16" if a.logits_bf16 else "f32", "top_k": top_k},
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("attn_decode_kernel (dec_attn_step_paged)" if a.paged
-                       else "attn_decode_kernel (dec_attn_step)"),
+            "kernel": f"attn_decode_kernel ({attn_entry})",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None,
@@ -436,6 +513,10 @@ def main(argv=None):
             "event_pair_median_us": round(per[len(per) // 2], 3), "launches": n_k,
             "algorithmic_bytes_per_launch": valid,
         },
+        "sampler": {"kernel": f"sample_topk_kernel ({samp_entry})", "top_k": top_k,
+                    "avg_launch_us": round(samp_us, 3),
+                    "avg_launch_us_method": f"HIP events around a captured graph of {n_k} "
+                                            f"launches, {k_reps} replays"},
         "checks": {"outputs_finite": out_ok, "tokens_in_range": tok_ok},
         "host_wall_s": round(wall, 4),
     }

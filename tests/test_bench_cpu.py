@@ -42,3 +42,16 @@ def test_counter_record_parses_and_is_consistent():
 def test_unknown_workload_has_no_traffic():
     rec, why = bench.counter_traffic("no_such_workload")
     assert rec is None and "no counter summary" in why
+
+
+def test_widened_attention_with_paged_cache_is_refused():
+    # key masks and bf16 outputs go with the static caches; refused before any GPU work
+    assert bench.main(["--paged", "64", "--cross-mask", "0.5"]) == 2
+    assert bench.main(["--paged", "64", "--out-bf16"]) == 2
+
+
+def test_variant_options_parse():
+    a = bench.parse(["--head-dim", "128", "--cross-mask", "0.3", "--mask-runs", "64",
+                     "--out-bf16", "--top-k", "250", "--logits-bf16"])
+    assert (a.head_dim, a.cross_mask, a.mask_runs, a.out_bf16, a.top_k, a.logits_bf16) == \
+        (128, 0.3, 64, True, 250, True)

@@ -109,3 +109,28 @@ def test_all_true_mask_changes_no_bit():
     r_s, r_c = hp.attn_step(w, d, ws=ws)
     assert np.array_equal(hp.host(o_c).view(np.uint32), hp.host(r_c).view(np.uint32))
     assert np.array_equal(hp.host(o_s).view(np.uint32), hp.host(r_s).view(np.uint32))
+
+
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_fully_masked_tiles_are_not_read(split, monkeypatch):
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    w, d, enc, mask = _masked_case(6)
+    mask[:, 64:192] = False             # two whole 64-key tiles of every sequence
+    for name in ("k_cross", "v_cross"):  # NaN there: a read of them would show
+        d[name][:, :, :, 64:192, :] = float("nan")
+    packed = _pack(mask)
+    ws = hp.workspace(w, w.self_cap, w.cross_cap)
+    o_s, o_c = hp.out_buf(w), hp.out_buf(w)
+    _ex(w, d, o_s, o_c, ws, mask=_dev(packed), words=packed.shape[1])
+    got = hp.host(o_c)
+    assert np.all(np.isfinite(got))
+    q = oattn.bf16_bits_to_f64(gen.queries(w, "cross"))
+    worst = 0.0
+    for layer in range(w.n_layers):
+        for b in range(w.batch):
+            K = oattn.bf16_bits_to_f64(gen.kv_rows(w, "cross", "k", layer, b, w.cross_cap))
+            V = oattn.bf16_bits_to_f64(gen.kv_rows(w, "cross", "v", layer, b, w.cross_cap))
+            for h in range(w.heads):
+                o = oattn.attend_masked(q[layer, b, h], K[h], V[h], enc[b], mask[b], w.scale)
+                worst = max(worst, hp.row_rel_err(got[layer, b, h], o))
+    assert worst <= BAR, worst

@@ -180,6 +180,9 @@ def test_cross_mask_and_bf16_outputs(split, monkeypatch):
     mask = rng.random((B, w.cross_cap)) < 0.4
     mask[2, :] = False                  # no attended key: zeros
     mask[1, 300:] = True                # bits past enc_len: ignored
+    mask[:, 32:96] = False              # two whole 32-key tiles: not read (NaN there)
+    for name in ("k_cross", "v_cross"):
+        d[name][:, :, :, 32:96, :] = float("nan")
     packed = _pack(mask)
     ws = hp.workspace(w, w.self_cap, w.cross_cap)
     o_s, o_c = hp.out_buf(w), hp.out_buf(w)
