@@ -51,18 +51,21 @@ def test_kept_set_matches_stable_argsort(seed):
 def test_probabilities_match_scipy_softmax(seed):
     rng = np.random.default_rng(200 + seed)
     x = (rng.standard_normal(1089) * 3).astype(np.float32).astype(np.float64)
-    for T in (0.05, 0.7, 1.0, 1.3, 25.0):
-        tok, kept, p, C, _ = S.sample_row(x, T, 50, 0.5)
-        ref = special.softmax(x[kept] / T)
-        assert np.allclose(p, ref, rtol=1e-12, atol=1e-300)
-        assert abs(math.fsum(p) - 1.0) < 1e-12
-        assert tok in kept
+    for k in (50, 250, 1089):
+        for T in (0.05, 0.7, 1.0, 1.3, 25.0):
+            tok, kept, p, C, _ = S.sample_row(x, T, k, 0.5)
+            assert len(kept) == k
+            ref = special.softmax(x[kept] / T)
+            assert np.allclose(p, ref, rtol=1e-12, atol=1e-300)
+            assert abs(math.fsum(p) - 1.0) < 1e-12
+            assert tok in kept
 
 
-def test_token_is_the_inverse_cdf_over_ascending_vocabulary():
+@pytest.mark.parametrize("k", [50, 250])
+def test_token_is_the_inverse_cdf_over_ascending_vocabulary(k):
     rng = np.random.default_rng(300)
     x = (rng.standard_normal(1089) * 3).astype(np.float32).astype(np.float64)
-    T, k = 0.9, 50
+    T = 0.9
     _, kept, _, _, _ = S.sample_row(x, T, k, 0.0)
     p = special.softmax(x[kept] / T)
     bounds = [math.fsum(p[:r + 1]) for r in range(len(kept))]   # independent prefix sums
