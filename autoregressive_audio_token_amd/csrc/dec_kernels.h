@@ -102,12 +102,15 @@ hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
 
 constexpr int kHeadWaves = 4;   // 8-row groups (one per wave) per workgroup
 constexpr int kHeadBT = 16;     // rows of h staged in LDS at a time
+constexpr int kHeadMfmaMinBatch = 3;   // batches from this size take the MFMA path
 
 struct HeadParams {
   const uint16_t* h;      // [B, D] bf16
   const uint16_t* W;      // [n_cb, V_stride, D] bf16
   float* logits;          // [B, n_cb, V_stride]; columns >= V_valid untouched
   int B, D, n_cb, V_valid, V_stride;
+  int force_gemv;         // 1: the vector-ALU kernel at every batch size (tests)
+  int mfma_cfg;           // MFMA path: 10 * row tiles + batch tiles per workgroup, 0: by B
 };
 
 struct EmbedParams {

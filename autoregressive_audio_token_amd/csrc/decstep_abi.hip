@@ -409,7 +409,7 @@ int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n
   if ((long long)B * n_cb * V_stride > (1LL << 40) || (long long)n_cb * V_stride > (1 << 24))
     return DEC_E_SHAPE;
   if (D != 512 && D != 768 && D != 1024 && D != 1536 && D != 2048) return DEC_E_UNSUPPORTED;
-  if ((long long)V_valid * D * 2 > (1LL << 31) - 1) return DEC_E_UNSUPPORTED;
+  if ((long long)(V_valid + 64) * D * 2 > (1LL << 31) - 1) return DEC_E_UNSUPPORTED;
   if (!aligned(h, 16) || !aligned(W, 16) || !aligned(logits, 4)) return DEC_E_ALIGN;
   dec::HeadParams p{};
   p.h = static_cast<const uint16_t*>(h);
@@ -420,6 +420,10 @@ int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n
   p.n_cb = n_cb;
   p.V_valid = V_valid;
   p.V_stride = V_stride;
+  // the MFMA path stores 4 logits at a time and addresses h with 32-bit offsets
+  p.force_gemv = env_int("DECSTEP_HEAD_GEMV", 0) || !aligned(logits, 16) || V_stride % 4 != 0 ||
+                 (long long)(B + 32) * D * 2 > (1LL << 31) - 1;
+  p.mfma_cfg = env_int("DECSTEP_HEAD_CFG", 0);  // 0: the measured policy
   const hipError_t e = dec::lm_head_launch(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }

@@ -26,6 +26,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
@@ -85,8 +87,121 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_kernel(HeadParams 
   }
 }
 
+// Batches of several rows: the same product on MFMA (v_mfma_f32_16x16x32_bf16).  A
+// workgroup owns RT tiles of 16 rows of one codebook; its 4 waves split D into
+// quarters, so a wave holds RT x 16 rows x D/4 of W (T k-steps of 32 per tile).  The A
+// operand is W (lane l: row l % 16, k (l / 16) * 8 .. + 8 of each 32-wide step), the B
+// operand h^T for 16 batch rows (lane l: batch row l % 16, the same k), so C holds rows
+// (l / 16) * 4 + i of batch row l % 16.  The k order inside a step is the same for A
+// and B, so the product is the plain dot product.  A pass covers NBT tiles of 16 batch
+// rows whose B fragments are all loaded with W, up front; the next pass's fragments are
+// in flight while a pass is reduced.  Rows of W at or past V_valid and rows of h at or
+// past B read as zero through their descriptors.  The four quarter sums of each output
+// tile meet in LDS and are added in wave order.
+template <int T, int RT, int NBT>
+__global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_mfma_kernel(HeadParams p) {
+  constexpr int D = kHeadWaves * 32 * T;
+  constexpr int NT = RT * NBT;  // output tiles of 16 x 16 per pass
+  __shared__ f32x4 s_c[kHeadWaves][NT][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  constexpr int ROWS = 16 * RT;
+  const int rgpc = (p.V_valid + ROWS - 1) / ROWS;  // row groups per codebook
+  const int c = blockIdx.x / rgpc;
+  const int v0 = (blockIdx.x - c * rgpc) * ROWS;
+  const int r = lane & 15;    // A row / B column within a tile
+  const int q = lane >> 4;    // 8-element k slice within a 32-wide step
+  const int k0 = wave * (D / kHeadWaves) + q * 8;
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.W + (size_t)c * p.V_stride * D), 0, p.V_valid * D * 2, kBufWord3);
+  u32x4 a[RT][T];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      a[rt][t] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, ((v0 + rt * 16 + r) * D + k0 + t * 32) * 2, 0, kBufNonTemporal);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.h), 0, p.B * D * 2, kBufWord3);
+  u32x4 hq[NBT][T];
+#pragma unroll
+  for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      hq[bt][t] = __builtin_amdgcn_raw_buffer_load_b128(rh, ((bt * 16 + r) * D + k0 + t * 32) * 2,
+                                                        0, 0);
+  for (int b0 = 0; b0 < p.B; b0 += 16 * NBT) {
+    f32x4 acc[NBT][RT];
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        acc[bt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[bt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[rt][t]), __builtin_bit_cast(bf16x8, hq[bt][t]),
+              acc[bt][rt], 0, 0, 0);
+      }
+    if (b0 + 16 * NBT < p.B) {  // the next pass's fragments (uniform branch)
+#pragma unroll
+      for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          hq[bt][t] = __builtin_amdgcn_raw_buffer_load_b128(
+              rh, ((b0 + (NBT + bt) * 16 + r) * D + k0 + t * 32) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) s_c[wave][bt * RT + rt][lane] = acc[bt][rt];
+    __syncthreads();
+    for (int tile = wave; tile < NT; tile += kHeadWaves) {  // wave w reduces tiles w, w + 4, ..
+      const f32x4 sum = ((s_c[0][tile][lane] + s_c[1][tile][lane]) + s_c[2][tile][lane]) +
+                        s_c[3][tile][lane];
+      const int b = b0 + (tile / RT) * 16 + r;
+      const int v = v0 + (tile % RT) * 16 + q * 4;  // rows v .. v + 3 of codebook c
+      if (b < p.B) {
+        float* out = p.logits + ((size_t)b * p.n_cb + c) * p.V_stride + v;
+        if (v + 3 < p.V_valid) {
+          *reinterpret_cast<f32x4*>(out) = sum;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v + i < p.V_valid) out[i] = sum[i];
+        }
+      }
+    }
+    __syncthreads();  // s_c is rewritten by the next pass
+  }
+}
+
+template <int T, int RT, int NBT>
+static void lm_head_mfma_go(const HeadParams& p, hipStream_t stream) {
+  const int blocks = p.n_cb * ((p.V_valid + 16 * RT - 1) / (16 * RT));
+  hipLaunchKernelGGL((lm_head_mfma_kernel<T, RT, NBT>), dim3(blocks), dim3(kHeadWaves * kWave), 0,
+                     stream, p);
+}
+
 template <int NSEG>
 static hipError_t lm_head_launch_n(const HeadParams& p, hipStream_t stream) {
+  if (p.B >= kHeadMfmaMinBatch && !p.force_gemv) {
+    constexpr int T = NSEG * 64 / (kHeadWaves * 32);
+    // Row tiles x batch tiles per workgroup, from measurement (D = 1024): one 16-row tile
+    // while the batch fits one batch tile (the most workgroups); beyond, four row tiles
+    // and two batch tiles per pass, so each load of h serves 64 rows (two row tiles at
+    // D > 1024, where four would not fit the register file).
+    int cfg = p.mfma_cfg;
+    if (cfg == 0) cfg = p.B <= 16 ? 11 : (T <= 8 ? 42 : 22);
+    switch (cfg) {
+      case 11: lm_head_mfma_go<T, 1, 1>(p, stream); break;
+      case 12: lm_head_mfma_go<T, 1, 2>(p, stream); break;
+      case 22: lm_head_mfma_go<T, 2, 2>(p, stream); break;
+      default: lm_head_mfma_go<T, 4, 2>(p, stream); break;
+    }
+    return hipGetLastError();
+  }
   const int groups = p.n_cb * ((p.V_valid + 7) / 8);
   const int blocks = (groups + kHeadWaves - 1) / kHeadWaves;
   hipLaunchKernelGGL(lm_head_kernel<NSEG>, dim3(blocks), dim3(kHeadWaves * kWave), 0, stream, p);

@@ -42,6 +42,8 @@ def parse(argv=None):
     ap.add_argument("--heads", action="store_true",
                     help="time the merged LM head (and the merged embedding sum) of the\n"
                          "workload's batch instead of the attention + sampling step")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="with --heads: the batch size (0: the workload's)")
     ap.add_argument("--eager", action="store_true",
                     help="run warmup + steps eager steps (no graph, no timing) and exit;\n"
                          "the launch sequence the hardware-counter runs profile")
@@ -110,6 +112,8 @@ def heads_bench(a, w):
     from workloads import configs, gen, device as wdev
 
     dev = torch.device("cuda:0")
+    if a.batch > 0:
+        w = dataclasses.replace(w, batch=a.batch)
     D, B, n_cb = configs.D_MODEL, w.batch, w.n_codebooks
     V, S = w.vocab_valid, w.vocab_stride
     alg = n_cb * V * D * 2 + B * D * 2 + B * n_cb * V * 4       # W valid rows, h, logits
@@ -146,6 +150,10 @@ def heads_bench(a, w):
         return e0.elapsed_time(e1) * 1e3 / (3 * n_k)
 
     head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
+    os.environ["DECSTEP_HEAD_GEMV"] = "1"      # the vector-ALU kernel, for comparison
+    gemv_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
+    del os.environ["DECSTEP_HEAD_GEMV"]
+    head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
     emb_us = timed(lambda i: dec.dec_embed_sum(toks, E, x, B, n_cb, S, D, stream))
     ok = bool(torch.isfinite(logits[:, :, :V]).all().item() and torch.isfinite(x).all().item())
     achieved = alg / (head_us * 1e-6) / 1e9
@@ -157,12 +165,15 @@ def heads_bench(a, w):
         "config": {"workload": w.name, "batch": B, "d_model": D, "codebooks": n_cb,
                    "vocab": V, "vocab_stride": S, "weight_sets": R,
                    "algorithmic_bytes_per_launch": alg},
-        "roofline": {"bound": "hbm", "kernel": "lm_head_kernel (dec_lm_head)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("lm_head_mfma_kernel" if B >= 3 else "lm_head_kernel") + " (dec_lm_head)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(head_us, 3),
                      "avg_launch_us_method": f"HIP events around a captured graph of {n_k} "
                                              f"launches, 3 replays"},
+        "lm_head_path": "mfma" if B >= 3 else "vector ALU (dot2)",
+        "vector_alu_kernel_us": round(gemv_us, 3),
         "embed_sum_us": round(emb_us, 3),
         "checks": {"outputs_finite": ok},
     }

@@ -29,11 +29,15 @@ def _bf16(rng, shape, std):
 
 
 @pytest.mark.parametrize("B,D", [(1, 1024), (3, 1024), (17, 512), (32, 1024), (2, 2048),
-                                 (5, 768), (1, 1536)])
-def test_lm_head_matches_oracle(B, D):
+                                 (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
+@pytest.mark.parametrize("path", ["default", "gemv"])
+def test_lm_head_matches_oracle(B, D, path, monkeypatch):
+    # default: the MFMA kernel from B = 2 on; gemv: the vector-ALU kernel at every B
+    if path == "gemv":
+        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
     n_cb, V, S = 9, configs.VOCAB_VALID, configs.VOCAB_PADDED
     rng = np.random.default_rng(1000 + B * 7 + D)
-    print(f"[lm_head] B={B} D={D}", flush=True)
+    print(f"[lm_head] B={B} D={D} path={path}", flush=True)
     h = _bf16(rng, (B, D), 1.0)
     W = _bf16(rng, (n_cb, S, D), 1.0 / 32)
     W[:, V:, :] = gen.BF16_NAN                       # padding rows: never read
@@ -48,6 +52,31 @@ def test_lm_head_matches_oracle(B, D):
     err = np.abs(got[:, :, :V] - want)
     assert np.all(err <= 2e-5 * absum), float(np.max(err / absum))
     print(f"  max err / sum|terms| = {float(np.max(err / absum)):.2e}", flush=True)
+
+
+@pytest.mark.parametrize("V", [1, 15, 16, 17, 1089])
+def test_lm_head_partial_row_groups_and_unaligned_output(V):
+    # a last group of 16 rows that is partly past V_valid; an output pointer that is only
+    # 4-byte aligned (the MFMA path's 16-byte stores are not allowed there)
+    B, D, n_cb = 4, 512, 3
+    S = V + (-V) % 8
+    rng = np.random.default_rng(V)
+    h = _bf16(rng, (B, D), 1.0)
+    W = _bf16(rng, (n_cb, S, D), 1.0 / 32)
+    W[:, V:, :] = gen.BF16_NAN
+    want = oheads.lm_head(h, W, V)
+    for offset in (0, 1):
+        buf = torch.full((B * n_cb * S + 4,), float(SENTINEL), dtype=torch.float32, device=hp.DEV)
+        logits = buf[offset:offset + B * n_cb * S]
+        dec.dec_lm_head(_dev(h), _dev(W), logits, B, D, n_cb, V, S)
+        got = hp.host(buf)[offset:offset + B * n_cb * S].reshape(B, n_cb, S)
+        assert np.all(got[:, :, V:] == SENTINEL), "padding columns written"
+        assert np.all(hp.host(buf)[:offset] == SENTINEL)
+        assert np.all(hp.host(buf)[offset + B * n_cb * S:] == SENTINEL)
+        hf = oattn.bf16_bits_to_f64(h)
+        Wf = oattn.bf16_bits_to_f64(W[:, :V])
+        absum = np.einsum("bd,cvd->bcv", np.abs(hf), np.abs(Wf))
+        assert np.all(np.abs(got[:, :, :V] - want) <= 2e-5 * absum)
 
 
 def test_lm_head_feeds_the_sampler_layout():
