@@ -11,9 +11,10 @@
 //     workgroup of kAttnWaves wavefronts streams a chunk in tile rounds: in
 //     each round every wave reads a 64-key tile (a key row of 64 bf16 is 128 B
 //     = 8 lanes x 16 B, so one dwordx4 load instruction covers 8 consecutive
-//     keys, 1 KiB, fully coalesced), and the next tile's K and V loads are in
-//     flight while the current tile is computed (double buffering).  There is
-//     no MFMA: the work is a GEMV, bound by HBM.
+//     keys, 1 KiB, fully coalesced; at head dim 128 a tile is 32 keys of 256 B,
+//     the same bytes), and the next tile's K and V loads are in flight while
+//     the current tile is computed (double buffering).  There is no MFMA: the
+//     work is a GEMV, bound by HBM.
 //   * Scores reduce across the 8 lanes of a key with DPP moves.  Each group of
 //     8 lanes keeps its own online-softmax state across the tiles (base 2, q
 //     pre-scaled by scale * log2 e, fp32), so a tile needs no cross-lane max.
