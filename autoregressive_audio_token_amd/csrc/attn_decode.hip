@@ -34,6 +34,8 @@
 //     each).  The work list is derived on the device from len[] (device
 //     resident, so a captured graph stays valid as lengths change), longest
 //     sequences first; a persistent, occupancy-sized grid walks it.
+#include <atomic>
+
 #include "dec_common.h"
 #include "dec_kernels.h"
 
@@ -610,9 +612,11 @@ long long attn_items_cap(const AttnParams& p) {
 }
 
 namespace {
+// Per-device launch facts, filled on first use.  Threads may launch concurrently, so the
+// fields are relaxed atomics: every writer stores the same value.
 struct DevInfo {
-  int cus = 0;
-  int occ[2][2][3] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
+  std::atomic<int> cus{0};
+  std::atomic<int> occ[2][2][3] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
 };
 DevInfo g_dev[64];
 
@@ -656,21 +660,21 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     DevInfo& di = g_dev[dev & 63];
-    if (di.cus == 0) {
-      int cus = 0;
+    int cus = di.cus.load(std::memory_order_relaxed);
+    if (cus == 0) {
       e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      di.cus = cus;
+      di.cus.store(cus, std::memory_order_relaxed);
     }
-    int occ = di.occ[dtype][wide][variant];
+    int occ = di.occ[dtype][wide][variant].load(std::memory_order_relaxed);
     if (occ == 0 || G > 64) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);
       if (e != hipSuccess) return e;
       if (occ < 1) occ = 1;
-      if (G <= 64) di.occ[dtype][wide][variant] = occ;
+      if (G <= 64) di.occ[dtype][wide][variant].store(occ, std::memory_order_relaxed);
     }
     const long long cap = attn_items_cap(p);
-    const long long want = (long long)di.cus * occ;
+    const long long want = (long long)cus * occ;
     blocks = (int)(want < cap ? want : cap);
   }
   if (blocks < 1) blocks = 1;
