@@ -95,15 +95,20 @@ __device__ __forceinline__ bool search2(const uint32_t (&key)[NS], int kk, int l
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Per wave: 256 histogram buckets, then one private word per lane that absorbs the
+// counts of keys outside the current prefix, so no atomic is predicated (a branch
+// around each one costs more than the add).
+constexpr int kHistWords = 256 + kWave;
+
 // Radix search for tau over NS slots per lane (absent slots: idx -1).  Every present
 // key lies in [lo, hi], so the bits above the highest bit where lo and hi differ are
 // shared and known.  Each pass resolves the next 8 bits: the keys that still match
 // the resolved prefix are counted into 256 LDS buckets (stored in descending bucket
 // order, so lane l holds buckets 255-4l..252-4l in one 16-byte read), a wave scan
-// turns the counts into "keys at or above this bucket", and a ballot picks the
-// bucket that holds the kk-th largest key.  Returns tau such that either exactly kk
-// keys are >= tau (an exact cut was found), or tau is the kk-th largest key; both
-// give the same kept set under the tie rule of select_kept.
+// turns the counts into "keys at or above this bucket", and a ballot picks the bucket
+// that holds the kk-th largest key.  Returns tau such that either exactly
+// kk keys are >= tau (an exact cut was found), or tau is the kk-th largest key; both
+// give the same kept set under the tie rule of select_kept.  hist: kHistWords words.
 template <int NS>
 __device__ __forceinline__ uint32_t radix_tau(const uint32_t (&key)[NS], const int (&idx)[NS],
                                               int kk, uint32_t lo, uint32_t hi, uint32_t* hist) {
@@ -114,6 +119,7 @@ __device__ __forceinline__ uint32_t radix_tau(const uint32_t (&key)[NS], const i
   uint32_t prefix = top == 31 ? 0u : (hi & ~((2u << top) - 1u));
   int above = 0;                                               // keys above the prefix range
   u32x4_t* h4 = reinterpret_cast<u32x4_t*>(hist);
+  uint32_t* const dummy = hist + 256 + lane;
   for (;;) {
     const int sh = top >= 7 ? top - 7 : 0;
     const uint32_t high = top == 31 ? 0u : ~((2u << top) - 1u);  // resolved bits
@@ -122,9 +128,10 @@ __device__ __forceinline__ uint32_t radix_tau(const uint32_t (&key)[NS], const i
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
-      if (idx[j] >= 0 && (key[j] & high) == prefix)
-        atomicAdd(&hist[255 - ((key[j] >> sh) & 0xFFu)], 1u);
+    for (int j = 0; j < NS; ++j) {
+      const bool in = idx[j] >= 0 && (key[j] & high) == prefix;
+      atomicAdd(in ? &hist[255 - ((key[j] >> sh) & 0xFFu)] : dummy, 1u);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -155,7 +162,7 @@ __device__ __forceinline__ uint32_t radix_tau(const uint32_t (&key)[NS], const i
 // Absent slots carry key 0 and idx -1.  Every present key is at least `lo`, and
 // the largest is `hi`.  Writes the kept (value, index) pairs in vocabulary order to
 // cval/cidx[0..kk) (lanes outside the kept set write a dummy slot, so no store is
-// predicated).  hist: 256 words of this wave's LDS, 16-byte aligned.
+// predicated).  hist: kHistWords words of this wave's LDS, 16-byte aligned.
 template <int NS>
 __device__ __forceinline__ void select_kept(const uint32_t (&key)[NS], const int (&idx)[NS], int kk,
                                             uint32_t lo, uint32_t hi, float* cval, int* cidx,
@@ -222,9 +229,12 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
   const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
   const float m = key_value(kmax);
   const bool greedy = T <= 0.f;
+  // e = 2^((x - m) * log2(e) / T): one multiply by a per-row factor and the hardware
+  // exponential per entry, in place of a division and expf
+  // (held finite for a denormal T, so the row maximum still gets (x - m) * c2 = 0)
+  const float c2 = fminf(1.4426950408889634f / T, 3.4e38f);
   float e[VPL], S[VPL];
   int pos[VPL];
-  float run = 0.f;  // sum of e over the slots before j
   int eq_before = 0, kept_before = 0;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
@@ -233,33 +243,41 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
     const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
     const unsigned long long km = __ballot(kept);
     pos[j] = kept ? kept_before + lanes_below(km) : -1;
-    e[j] = kept && !greedy ? expf((key_value(key[j]) - m) / T) : 0.f;
-    S[j] = run + wave_inclusive_sum(e[j], lane);
-    run = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S[j]), kWave - 1));
+    e[j] = kept && !greedy ? __builtin_amdgcn_exp2f((key_value(key[j]) - m) * c2) : 0.f;
     eq_before += __popcll(eqm);
     kept_before += __popcll(km);
   }
+  // the slot scans are independent; only their totals chain: S[j] = run_j + scan_j with
+  // run_{j+1} = run_j + scan_j[63], the additions of a running sum in vocabulary order
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) S[j] = wave_inclusive_sum(e[j], lane);
+  float run = 0.f;  // sum of e over the slots before j
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S[j]), kWave - 1));
+    S[j] = run + S[j];
+    run = run + t;
+  }
   // run is now the inclusive sum at the last kept entry (later terms are zeros)
   const float Z = run;
+  const float rZ = 1.f / Z;  // C = S * rZ and p = e * rZ: within 1.5 ulp of S / Z, e / Z
   int token = -1;  // the sampled index, before the delay mask
+  unsigned long long hit[VPL];
   if (greedy) {  // the lowest index holding the largest key
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const unsigned long long mk = __ballot(idx[j] >= 0 && key[j] == kmax);
-      if (token < 0 && mk) token = j * kWave + __ffsll(mk) - 1;
-    }
+    for (int j = 0; j < VPL; ++j) hit[j] = __ballot(idx[j] >= 0 && key[j] == kmax);
   } else {
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const unsigned long long mk = __ballot(pos[j] >= 0 && u < S[j] / Z);
-      if (token < 0 && mk) token = j * kWave + __ffsll(mk) - 1;
-    }
-    if (token < 0) {  // rounding left u >= C_last: the last kept entry
+    for (int j = 0; j < VPL; ++j) hit[j] = __ballot(pos[j] >= 0 && u < S[j] * rZ);
+  }
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const unsigned long long mk = __ballot(pos[j] == kk - 1);
-        if (mk) token = j * kWave + __ffsll(mk) - 1;
-      }
+  for (int j = VPL - 1; j >= 0; --j)  // the first slot with a hit wins
+    if (hit[j]) token = j * kWave + __ffsll(hit[j]) - 1;
+  if (token < 0) {  // rounding left u >= C_last: the last kept entry
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const unsigned long long mk = __ballot(pos[j] == kk - 1);
+      if (mk) token = j * kWave + __ffsll(mk) - 1;
     }
   }
   if (lane == 0) p.tokens[row] = started ? token : p.fill;
@@ -269,7 +287,7 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
   for (int j = 0; j < VPL; ++j) {
     if (pos[j] < 0) continue;
     if (oi != nullptr) oi[pos[j]] = idx[j];
-    if (op != nullptr) op[pos[j]] = greedy ? (idx[j] == token ? 1.f : 0.f) : e[j] / Z;
+    if (op != nullptr) op[pos[j]] = greedy ? (idx[j] == token ? 1.f : 0.f) : e[j] * rZ;
   }
   for (int t = kk + lane; t < p.top_k; t += kWave) {
     if (oi != nullptr) oi[t] = -1;
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   __shared__ float s_val[kSampWaves][2 * kWave];
   __shared__ int s_idx[kSampWaves][2 * kWave];
   __shared__ uint2 s_surv[kSampWaves][kSurvCap + kWave];
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSampWaves][256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSampWaves][kHistWords];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
