@@ -304,7 +304,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // uniform per wave; said explicitly so the sequence, its pointers and its buffer
+  // descriptors stay in scalar registers (a descriptor the compiler must treat as
+  // per-lane turns every buffer load into a readfirstlane loop)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int B = p.B;
   const int G = p.nseg * B;
   const int NLH = p.NL * p.H;

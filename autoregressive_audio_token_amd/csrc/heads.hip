@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_kernel(HeadParams 
   __shared__ u32x4 s_h[kHeadBT * D / 8];  // kHeadBT rows of h, bf16
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int grp = lane >> 3;  // row within the wave's 8
   const int sl = lane & 7;    // 16-byte slice of each 128-byte segment
   const int rgpc = (p.V_valid + 7) >> 3;  // 8-row groups per codebook
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_mfma_kernel(HeadPa
   constexpr int NT = RT * NBT;  // output tiles of 16 x 16 per pass
   __shared__ f32x4 s_c[kHeadWaves][NT][kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   constexpr int ROWS = 16 * RT;
   const int rgpc = (p.V_valid + ROWS - 1) / ROWS;  // row groups per codebook
   const int c = blockIdx.x / rgpc;

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSampWaves][kHistWords];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int rows = p.B * p.n_cb;
   const int row = blockIdx.x * kSampWaves + wave;
   if (row >= rows) return;  // uniform per wave; waves never wait on each other
