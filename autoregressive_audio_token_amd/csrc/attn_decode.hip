@@ -467,11 +467,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       kp += wave_sidx * (size_t)S.L_cap * HD;
       vp += wave_sidx * (size_t)S.L_cap * HD;
     }
-    // static: one descriptor over the whole valid prefix
+    // static: one descriptor over the whole valid prefix (paged: none, so no rows).  A
+    // tile that must move no bytes is addressed at row `none`, the end of that range:
+    // every lane is out of range, reads zero and makes no memory request.
     const __amdgpu_buffer_rsrc_t rk_seq = rows_rsrc(kp, paged ? 0 : n, kRowBytes);
     const __amdgpu_buffer_rsrc_t rv_seq = rows_rsrc(vp, paged ? 0 : n, kRowBytes);
-    const __amdgpu_buffer_rsrc_t rk_none = rows_rsrc(kp, 0, kRowBytes);  // no rows: no traffic
-    const __amdgpu_buffer_rsrc_t rv_none = rows_rsrc(vp, 0, kRowBytes);
+    const int none = paged ? 0 : n;
     float fm = 0.f, fl = 0.f, fa = 0.f;  // running fold (combining threads)
     const T* qp = static_cast<const T*>(S.q) + wave_sidx * HD + dl * EPL;
 
@@ -490,15 +491,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           blk_of = S.table[(size_t)b * S.table_stride + ((cb + lane * kStep) >> S.bs_log2)];
         auto addr = [&](int t) -> TileAddr {
           const int base = cb + t * kStep;
-          // past this wave's tiles of the chunk: a descriptor with no rows, so the
-          // pipeline's last prefetch moves no bytes (the next chunk loads its own)
-          if (t >= nt) return {rk_none, rv_none, 0, 0ull};
+          // past this wave's tiles of the chunk: out of range, so the pipeline's last
+          // prefetch moves no bytes (the next chunk loads its own)
+          if (t >= nt) return {rk_seq, rv_seq, none, 0ull};
           uint64_t keep = ~0ull;
           if (EX && S.mask != nullptr) {  // the tile's KPT mask bits (uniform)
             const uint32_t* mw = S.mask + (size_t)b * S.mask_words + (base >> 5);
             keep = KPT == 64 ? *reinterpret_cast<const uint64_t*>(mw) : (uint64_t)*mw;
             // no attended key in the tile: nothing to read (every score is masked)
-            if (keep == 0ull) return {rk_none, rv_none, 0, 0ull};
+            if (keep == 0ull) return {rk_seq, rv_seq, none, 0ull};
           }
           if (!paged) return {rk_seq, rv_seq, base, keep};
           const int bs = 1 << S.bs_log2;

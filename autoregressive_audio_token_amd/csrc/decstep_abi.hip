@@ -100,9 +100,10 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   }
   if (!hd_ok(hd)) return DEC_E_UNSUPPORTED;
   if (nseg * B > dec::kAttnMaxGroups) return DEC_E_UNSUPPORTED;
-  for (int s = 0; s < nseg; ++s) {  // one sequence's static cache: 32-bit byte offsets
+  for (int s = 0; s < nseg; ++s) {  // one sequence's static cache (and one tile past its
+    // end, where no-traffic loads are addressed): 32-bit byte offsets
     const long long seq_bytes = (long long)segs[s].L_cap * hd * (dtype == DEC_BF16 ? 2 : 4);
-    if (segs[s].table == nullptr && seq_bytes > 0x7FFFFFFFLL) return DEC_E_UNSUPPORTED;
+    if (segs[s].table == nullptr && seq_bytes + 65536 > 0x7FFFFFFFLL) return DEC_E_UNSUPPORTED;
   }
   for (int s = 0; s < nseg; ++s) {
     if (!aligned(segs[s].q, 16) || !aligned(segs[s].k, 16) || !aligned(segs[s].v, 16) ||
