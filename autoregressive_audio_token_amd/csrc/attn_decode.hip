@@ -9,12 +9,13 @@
 // Split-K flash-decode, arranged for CDNA4:
 //   * A sequence of n valid keys is cut into chunks of kAttnChunk keys.  A
 //     workgroup of kAttnWaves wavefronts streams a chunk in tile rounds: in
-//     each round every wave reads a 64-key tile (a key row of 64 bf16 is 128 B
+//     each round every wave reads a 32-key tile (a key row of 64 bf16 is 128 B
 //     = 8 lanes x 16 B, so one dwordx4 load instruction covers 8 consecutive
-//     keys, 1 KiB, fully coalesced; at head dim 128 a tile is 32 keys of 256 B,
+//     keys, 1 KiB, fully coalesced; at head dim 128 a tile is 16 keys of 256 B,
 //     the same bytes), and the next tile's K and V loads are in flight while
-//     the current tile is computed (double buffering).  There is no MFMA: the
-//     work is a GEMV, bound by HBM.
+//     the current tile is computed (double buffering).  Tiles of this size keep
+//     the kernel at three waves per SIMD.  There is no MFMA: the work is a
+//     GEMV, bound by HBM.
 //   * Scores reduce across the 8 lanes of a key with DPP moves.  Each group of
 //     8 lanes keeps its own online-softmax state across the tiles (base 2, q
 //     pre-scaled by scale * log2 e, fp32), so a tile needs no cross-lane max.
@@ -195,7 +196,7 @@ __device__ __forceinline__ void fold_chunk(bool first, float mc, float lc, float
 }
 
 // One wave's view of a tile of KPT keys: NLD loads per operand, each covering KPL keys.
-// A tile holds the same bytes at either head dim (64 keys of 64, 32 keys of 128).
+// A tile holds the same bytes at either head dim (32 keys of 64, 16 keys of 128).
 template <typename T, int HD>
 struct Tile {
   static constexpr int EPL = KvTraits<T>::kElemsPerLoad;  // elements per lane per load
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   constexpr int TPC = attn_tiles_per_chunk(HD);
   constexpr int PS = attn_part_stride(HD);
   static_assert(kAttnThreads % HD == 0, "whole sequences per combining pass");
-  static_assert(!EX || KPT == 32 || KPT == 64, "a tile's mask bits are one or two whole words");
+  static_assert(!EX || KPT == 16 || KPT == 32 || KPT == 64, "a tile's mask bits lie in whole words");
 
   extern __shared__ int s_dyn[];  // [G] lengths, [G] order, [G+1] item prefix
   __shared__ float s_acc[kAttnWaves][HD];
@@ -489,6 +490,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
         int blk_of = 0;
         if (paged && lane < nt)
           blk_of = S.table[(size_t)b * S.table_stride + ((cb + lane * kStep) >> S.bs_log2)];
+        // key masks: lane i < nt holds the mask bits of the wave's tile i in this chunk, so
+        // a tile's bits are a register read, not a load on its address path
+        uint32_t mask_lo = ~0u, mask_hi = ~0u;
+        if (EX && S.mask != nullptr && lane < nt) {
+          const int base_i = cb + lane * kStep;
+          const uint32_t* mw = S.mask + (size_t)b * S.mask_words + (base_i >> 5);
+          if (KPT == 64) {
+            mask_lo = mw[0];
+            mask_hi = mw[1];
+          } else {
+            mask_lo = (mw[0] >> (base_i & 31)) & (KPT == 32 ? 0xFFFFFFFFu : 0xFFFFu);
+          }
+        }
         auto addr = [&](int t) -> TileAddr {
           const int base = cb + t * kStep;
           // past this wave's tiles of the chunk: out of range, so the pipeline's last
@@ -496,8 +510,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           if (t >= nt) return {rk_seq, rv_seq, none, 0ull};
           uint64_t keep = ~0ull;
           if (EX && S.mask != nullptr) {  // the tile's KPT mask bits (uniform)
-            const uint32_t* mw = S.mask + (size_t)b * S.mask_words + (base >> 5);
-            keep = KPT == 64 ? *reinterpret_cast<const uint64_t*>(mw) : (uint64_t)*mw;
+            keep = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mask_lo, t);
+            if (KPT == 64) keep |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mask_hi, t) << 32;
             // no attended key in the tile: nothing to read (every score is masked)
             if (keep == 0ull) return {rk_seq, rv_seq, none, 0ull};
           }

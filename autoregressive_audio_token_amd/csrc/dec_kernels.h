@@ -15,7 +15,7 @@ namespace dec {
 constexpr int kAttnWaves = DEC_ATTN_WAVES;          // waves per workgroup
 constexpr int kAttnThreads = 64 * kAttnWaves;
 #ifndef DEC_ATTN_TILE_KEYS
-#define DEC_ATTN_TILE_KEYS 64
+#define DEC_ATTN_TILE_KEYS 32
 #endif
 constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile at head
                                                     // dim 64 (at 128: half, same bytes)

@@ -110,7 +110,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
         !aligned(segs[s].len, 4) || !aligned(segs[s].out, segs[s].out_bf16 ? 2 : 4))
       return DEC_E_ALIGN;
     if (segs[s].mask != nullptr) {
-      // every 64-key tile reads two whole words
+      // whole 64-bit words per 64 keys: a tile never reads past the row
       const long long need = 2LL * ((segs[s].L_cap + 63) / 64);
       if (segs[s].mask_words < need || segs[s].mask_words % 2 != 0) return DEC_E_SHAPE;
       if (segs[s].table != nullptr) return DEC_E_UNSUPPORTED;  // masks go with static caches

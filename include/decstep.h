@@ -125,9 +125,8 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
  *               hidden by an attention mask).  Bit j % 32 of word j / 32 of row b
  *               set = key j attended.  Keys j < enc_len[b] with their bit set
  *               take part; a row with none outputs zeros.  mask_words must be
- *               even and at least 2 * ceil(L_cap_cross / 64) (a tile reads whole
- *               words: two per 64 keys at hd 64, one per 32 keys at hd 128);
- *               8-byte aligned.  A tile with no attended key is not read; the
+ *               even and at least 2 * ceil(L_cap_cross / 64) (a tile reads the
+ *               whole words that hold its keys' bits); 8-byte aligned.  A tile with no attended key is not read; the
  *               other keys of a tile that has one are read and weighted zero, so
  *               masked keys below enc_len[b] must hold finite values.
  *   out_dtype   DEC_F32 (float outputs, as dec_attn_step) or DEC_BF16 (outputs
@@ -156,7 +155,7 @@ int dec_attn_step_ex(const void* q_self, const void* k_self, const void* v_self,
  *                table for every layer and head)
  *   len          [B] int32, clamped to [0, max_blocks * block_size]
  *   out          [n_layers, B, H, hd] float32
- * block_size: a power of two, at least 64 (a tile, 64 keys at hd 64 and 32 at
+ * block_size: a power of two, at least 64 (a tile, 32 keys at hd 64 and 16 at
  * hd 128, never crosses a block),
  * else DEC_E_UNSUPPORTED.  Workspace: dec_attn_workspace_bytes with
  * L_cap_self = max_blocks * block_size.  Device-side: a table entry outside

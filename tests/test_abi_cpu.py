@@ -208,7 +208,7 @@ def test_attention_ex_host_validation():
                             a["mask"], a["words"], a["Lc"], a["out"], 24, 1, 16, 64, 0, a["od"],
                             ctypes.c_float(0.125), A, 1 << 30, None)
     assert ex(od=3) == D.DEC_E_DTYPE
-    assert ex(words=30) == D.DEC_E_SHAPE        # fewer than 2 words per 64-key tile
+    assert ex(words=30) == D.DEC_E_SHAPE        # fewer than 2 words per 64 keys
     assert ex(words=33) == D.DEC_E_SHAPE        # odd
     assert ex(mask=A + 4) == D.DEC_E_ALIGN      # each tile reads an aligned 64-bit pair
     assert ex(out=A + 2, od=1) == D.DEC_E_ALIGN  # fp32 outputs need 4-byte alignment

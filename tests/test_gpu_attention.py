@@ -80,8 +80,8 @@ def test_parity_long_output_selected_steps():
             _check("cross", w, d, o_c, src, rows, d["cross_len_host"])
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 1000, 1023, 1024, 1025, 2047, 2048, 2049,
-                               3071, 4095, 4096])
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 127, 1000, 1023, 1024, 1025, 2047,
+                               2048, 2049, 3071, 4095, 4096])
 def test_ragged_lengths_and_chunk_edges(n):
     w = configs.MINI_V1
     lens = np.array([n], dtype=np.int32)

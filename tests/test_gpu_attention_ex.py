@@ -115,7 +115,7 @@ def test_all_true_mask_changes_no_bit():
 def test_fully_masked_tiles_are_not_read(split, monkeypatch):
     monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
     w, d, enc, mask = _masked_case(6)
-    mask[:, 64:192] = False             # two whole 64-key tiles of every sequence
+    mask[:, 64:192] = False             # whole tiles (32-key) of every sequence
     for name in ("k_cross", "v_cross"):  # NaN there: a read of them would show
         d[name][:, :, :, 64:192, :] = float("nan")
     packed = _pack(mask)

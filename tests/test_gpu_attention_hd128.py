@@ -1,7 +1,7 @@
 """GPU parity of attention at head dim 128, through the C ABI.
 
-At head dim 128 a tile is 32 keys of 256 bytes (the bytes of a 64-key tile at head
-dim 64), a chunk is 8 tile rounds, a score reduces over 16 lanes (bf16) or 32 (fp32),
+At head dim 128 a tile is 16 keys of 256 bytes (the bytes of a 32-key tile at head
+dim 64), a chunk is 16 tile rounds, a score reduces over 16 lanes (bf16) or 32 (fp32),
 and short sequences pack at most two to a workgroup.  Bars as at head dim 64:
 * every output row within 2e-3 relative (max-norm) of the oracle, and within 1e-4 at
   these moderate score magnitudes (an fp32 dot product of 128 terms and an online
@@ -71,8 +71,8 @@ def test_parity_full(base):
     _check("cross", w, o_c, src, rows, c_len)
 
 
-@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1023, 1024, 1025,
-                               2049, 4095, 4096])
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1023, 1024,
+                               1025, 2049, 4095, 4096])
 @pytest.mark.parametrize("split", ["1", "0"])
 def test_ragged_lengths_both_schedules(n, split, monkeypatch):
     monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
@@ -180,7 +180,7 @@ def test_cross_mask_and_bf16_outputs(split, monkeypatch):
     mask = rng.random((B, w.cross_cap)) < 0.4
     mask[2, :] = False                  # no attended key: zeros
     mask[1, 300:] = True                # bits past enc_len: ignored
-    mask[:, 32:96] = False              # two whole 32-key tiles: not read (NaN there)
+    mask[:, 32:96] = False              # whole 16-key tiles: not read (NaN there)
     for name in ("k_cross", "v_cross"):
         d[name][:, :, :, 32:96, :] = float("nan")
     packed = _pack(mask)
