@@ -19,6 +19,8 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 #endif
 constexpr int kAttnKeysPerTile = DEC_ATTN_TILE_KEYS;  // keys one wave loads per tile at head
                                                     // dim 64 (at 128: half, same bytes)
+constexpr int kAttnMinBlockKeys = 64;               // paged cache: smallest block (keys)
+static_assert(kAttnKeysPerTile <= kAttnMinBlockKeys, "a tile never crosses a paged block");
 #ifndef DEC_ATTN_CHUNK
 #define DEC_ATTN_CHUNK 1024
 #endif

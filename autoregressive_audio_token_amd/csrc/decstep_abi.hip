@@ -93,7 +93,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     if (a.n_blocks < 1 || a.table_stride < 1) return DEC_E_SHAPE;
     if ((long long)NL * a.n_blocks * H * a.block_size * row > (1LL << 46)) return DEC_E_SHAPE;
     if ((long long)B * a.table_stride > (1LL << 30)) return DEC_E_SHAPE;
-    if (!is_pow2(a.block_size) || a.block_size < dec::kAttnKeysPerTile ||
+    if (!is_pow2(a.block_size) || a.block_size < dec::kAttnMinBlockKeys ||
         a.block_size > (1 << 20))
       return DEC_E_UNSUPPORTED;
     if (!aligned(a.table, 4)) return DEC_E_ALIGN;
