@@ -87,12 +87,21 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_kernel(HeadParams 
   }
 }
 
+// Orders one wave's LDS writes before its later LDS reads (and reads before later
+// writes) of lanes other than its own; LDS executes a wave's operations in order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Batches of several rows: the same product on MFMA (v_mfma_f32_16x16x32_bf16).  A
 // workgroup owns RT tiles of 16 rows of one codebook; its 4 waves split D into
-// quarters, so a wave holds RT x 16 rows x D/4 of W (T k-steps of 32 per tile).  The A
-// operand is W (lane l: row l % 16, k (l / 16) * 8 .. + 8 of each 32-wide step), the B
-// operand h^T for 16 batch rows (lane l: batch row l % 16, the same k), so C holds rows
-// (l / 16) * 4 + i of batch row l % 16.  The k order inside a step is the same for A
+// quarters, so a wave holds RT x 16 rows x D/4 of W (T k-steps of 32 per tile), read in
+// whole cache lines and rearranged through LDS.  The A operand is W (lane l: row
+// l % 16, k (l / 16) * 8 .. + 8 of each 32-wide step), the B operand h^T for 16 batch
+// rows (lane l: batch row l % 16, the same k), so C holds rows (l / 16) * 4 + i of
+// batch row l % 16.  The k order inside a step is the same for A
 // and B, so the product is the plain dot product.  A pass covers NBT tiles of 16 batch
 // rows whose B fragments are all loaded with W, up front; the next pass's fragments are
 // in flight while a pass is reduced.  Rows of W at or past V_valid and rows of h at or
@@ -103,6 +112,7 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_mfma_kernel(HeadPa
   constexpr int D = kHeadWaves * 32 * T;
   constexpr int NT = RT * NBT;  // output tiles of 16 x 16 per pass
   __shared__ f32x4 s_c[kHeadWaves][NT][kWave];
+  __shared__ u32x4 s_w[kHeadWaves][T / 2][128];  // per wave: 16 rows x 8 chunks per step pair
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   constexpr int ROWS = 16 * RT;
@@ -115,13 +125,21 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_mfma_kernel(HeadPa
 
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.W + (size_t)c * p.V_stride * D), 0, p.V_valid * D * 2, kBufWord3);
+  // W is read in whole 128-byte lines, 8 consecutive lanes to a line: load t gives lane
+  // l row (l >> 3) + 8 * (t & 1), columns (t >> 1) * 64 + (l & 7) * 8 .. + 8 of the
+  // wave's quarter.  Each tile of 16 rows then passes through the wave's own slice of
+  // LDS into the A layout.  A pair of loads covers 16 rows x 8 chunks of 16 bytes; the
+  // chunk of row R sits at position chunk ^ swz(R), which puts the 8 chunks of a row
+  // (the writes) and one chunk of 16 rows (the reads) in distinct bank groups.
+  static_assert(T % 2 == 0, "W loads come in pairs of 32-wide steps");
+  const int wl = (lane >> 3) * D + wave * (D / kHeadWaves) + (lane & 7) * 8;
   u32x4 a[RT][T];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int t = 0; t < T; ++t)
       a[rt][t] = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, ((v0 + rt * 16 + r) * D + k0 + t * 32) * 2, 0, kBufNonTemporal);
+          rw, ((v0 + rt * 16 + 8 * (t & 1)) * D + wl + (t >> 1) * 64) * 2, 0, kBufNonTemporal);
   const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.h), 0, p.B * D * 2, kBufWord3);
   u32x4 hq[NBT][T];
@@ -131,6 +149,24 @@ __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_mfma_kernel(HeadPa
     for (int t = 0; t < T; ++t)
       hq[bt][t] = __builtin_amdgcn_raw_buffer_load_b128(rh, ((bt * 16 + r) * D + k0 + t * 32) * 2,
                                                         0, 0);
+  u32x4* const tile = &s_w[wave][0][0];
+  auto swz = [](int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; };
+  int put[2], get[2];  // chunk slots within a pair: written by load parity, read by step parity
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int wr = (lane >> 3) + 8 * h;
+    put[h] = wr * 8 + ((lane & 7) ^ swz(wr));
+    get[h] = r * 8 + ((h * 4 + q) ^ swz(r));
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (rt > 0) wave_lds_sync();  // the previous tile's reads are done before the writes
+#pragma unroll
+    for (int t = 0; t < T; ++t) tile[(t >> 1) * 128 + put[t & 1]] = a[rt][t];
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < T; ++t) a[rt][t] = tile[(t >> 1) * 128 + get[t & 1]];
+  }
   for (int b0 = 0; b0 < p.B; b0 += 16 * NBT) {
     f32x4 acc[NBT][RT];
 #pragma unroll

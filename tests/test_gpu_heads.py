@@ -28,16 +28,9 @@ def _bf16(rng, shape, std):
     return gen.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
 
 
-@pytest.mark.parametrize("B,D", [(1, 1024), (3, 1024), (17, 512), (32, 1024), (2, 2048),
-                                 (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
-@pytest.mark.parametrize("path", ["default", "gemv"])
-def test_lm_head_matches_oracle(B, D, path, monkeypatch):
-    # default: the MFMA kernel from B = 2 on; gemv: the vector-ALU kernel at every B
-    if path == "gemv":
-        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
+def _check_lm_head(B, D, seed):
     n_cb, V, S = 9, configs.VOCAB_VALID, configs.VOCAB_PADDED
-    rng = np.random.default_rng(1000 + B * 7 + D)
-    print(f"[lm_head] B={B} D={D} path={path}", flush=True)
+    rng = np.random.default_rng(seed)
     h = _bf16(rng, (B, D), 1.0)
     W = _bf16(rng, (n_cb, S, D), 1.0 / 32)
     W[:, V:, :] = gen.BF16_NAN                       # padding rows: never read
@@ -52,6 +45,27 @@ def test_lm_head_matches_oracle(B, D, path, monkeypatch):
     err = np.abs(got[:, :, :V] - want)
     assert np.all(err <= 2e-5 * absum), float(np.max(err / absum))
     print(f"  max err / sum|terms| = {float(np.max(err / absum)):.2e}", flush=True)
+
+
+@pytest.mark.parametrize("B,D", [(1, 1024), (3, 1024), (17, 512), (32, 1024), (2, 2048),
+                                 (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
+@pytest.mark.parametrize("path", ["default", "gemv"])
+def test_lm_head_matches_oracle(B, D, path, monkeypatch):
+    # default: the MFMA kernel from B = 3 on; gemv: the vector-ALU kernel at every B
+    if path == "gemv":
+        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
+    print(f"[lm_head] B={B} D={D} path={path}", flush=True)
+    _check_lm_head(B, D, 1000 + B * 7 + D)
+
+
+@pytest.mark.parametrize("B,D", [(3, 512), (20, 768), (40, 1024), (35, 1536), (19, 2048)])
+@pytest.mark.parametrize("cfg", [11, 12, 22, 42])
+def test_lm_head_every_mfma_tiling(B, D, cfg, monkeypatch):
+    # each row-tile x batch-tile choice of the MFMA kernel, at every model width: partial
+    # batch tiles, several passes over the batch, the last row group partly past V_valid
+    monkeypatch.setenv("DECSTEP_HEAD_CFG", str(cfg))
+    print(f"[lm_head mfma] B={B} D={D} cfg={cfg}", flush=True)
+    _check_lm_head(B, D, 2000 + B * 7 + D + cfg)
 
 
 @pytest.mark.parametrize("V", [1, 15, 16, 17, 1089])
