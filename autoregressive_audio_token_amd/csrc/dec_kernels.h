@@ -104,7 +104,6 @@ hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
 
 constexpr int kHeadWaves = 4;   // 8-row groups (one per wave) per workgroup
 constexpr int kHeadBT = 16;     // rows of h staged in LDS at a time
-constexpr int kHeadMfmaMinBatch = 3;   // batches from this size take the MFMA path
 
 struct HeadParams {
   const uint16_t* h;      // [B, D] bf16

@@ -222,14 +222,15 @@ static void lm_head_mfma_go(const HeadParams& p, hipStream_t stream) {
 
 template <int NSEG>
 static hipError_t lm_head_launch_n(const HeadParams& p, hipStream_t stream) {
-  if (p.B >= kHeadMfmaMinBatch && !p.force_gemv) {
+  if (!p.force_gemv) {
     constexpr int T = NSEG * 64 / (kHeadWaves * 32);
-    // Row tiles x batch tiles per workgroup, from measurement (D = 1024): one 16-row tile
-    // while the batch fits one batch tile (the most workgroups); beyond, four row tiles
-    // and two batch tiles per pass, so each load of h serves 64 rows (two row tiles at
-    // D > 1024, where four would not fit the register file).
+    // Row tiles x batch tiles per workgroup, from measurement at every width: one 16-row
+    // tile up to 12 batch rows (the most workgroups, which is what a weight-bound
+    // product needs); beyond, four row tiles and two batch tiles per pass, so each load
+    // of h serves 64 rows of W.  The MFMA kernel is the faster one from B = 1 on (W is
+    // read once either way; its loads are whole lines).
     int cfg = p.mfma_cfg;
-    if (cfg == 0) cfg = p.B <= 16 ? 11 : (T <= 8 ? 42 : 22);
+    if (cfg == 0) cfg = p.B <= 12 ? 11 : 42;
     switch (cfg) {
       case 11: lm_head_mfma_go<T, 1, 1>(p, stream); break;
       case 12: lm_head_mfma_go<T, 1, 2>(p, stream); break;

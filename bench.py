@@ -42,6 +42,8 @@ def parse(argv=None):
     ap.add_argument("--heads", action="store_true",
                     help="time the merged LM head (and the merged embedding sum) of the\n"
                          "workload's batch instead of the attention + sampling step")
+    ap.add_argument("--d-model", type=int, default=0, choices=(0, 512, 768, 1024, 1536, 2048),
+                    help="with --heads: the model width (0: the workload's, 1024)")
     ap.add_argument("--batch", type=int, default=0,
                     help="with --heads: the batch size (0: the workload's)")
     ap.add_argument("--eager", action="store_true",
@@ -114,7 +116,7 @@ def heads_bench(a, w):
     dev = torch.device("cuda:0")
     if a.batch > 0:
         w = dataclasses.replace(w, batch=a.batch)
-    D, B, n_cb = configs.D_MODEL, w.batch, w.n_codebooks
+    D, B, n_cb = a.d_model or configs.D_MODEL, w.batch, w.n_codebooks
     V, S = w.vocab_valid, w.vocab_stride
     alg = n_cb * V * D * 2 + B * D * 2 + B * n_cb * V * 4       # W valid rows, h, logits
     w_alloc = n_cb * S * D * 2
@@ -166,13 +168,13 @@ def heads_bench(a, w):
                    "vocab": V, "vocab_stride": S, "weight_sets": R,
                    "algorithmic_bytes_per_launch": alg},
         "roofline": {"bound": "hbm",
-                     "kernel": ("lm_head_mfma_kernel" if B >= 3 else "lm_head_kernel") + " (dec_lm_head)",
+                     "kernel": "lm_head_mfma_kernel (dec_lm_head)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(head_us, 3),
                      "avg_launch_us_method": f"HIP events around a captured graph of {n_k} "
                                              f"launches, 3 replays"},
-        "lm_head_path": "mfma" if B >= 3 else "vector ALU (dot2)",
+        "lm_head_path": "mfma",
         "vector_alu_kernel_us": round(gemv_us, 3),
         "embed_sum_us": round(emb_us, 3),
         "checks": {"outputs_finite": ok},

@@ -267,10 +267,10 @@ int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
  *           v >= V_valid are left untouched
  * No bias.  fp32 accumulation.  D one of 512, 768, 1024, 1536, 2048, else
  * DEC_E_UNSUPPORTED; (V_valid + 64) * D * 2 below 2^31 bytes; h and W 16-byte
- * aligned, logits 4-byte aligned.  Device pointers, caller-owned.  From B = 3 the
- * product runs on MFMA when logits is 16-byte aligned and V_stride a multiple of 4
- * (otherwise, and below B = 3, on the vector ALU); both round differently but stay
- * within the same fp32 accumulation bound. */
+ * aligned, logits 4-byte aligned.  Device pointers, caller-owned.  The product
+ * runs on MFMA when logits is 16-byte aligned, V_stride a multiple of 4 and
+ * (B + 32) * D * 2 below 2^31 bytes (otherwise on the vector ALU); both round
+ * differently but stay within the same fp32 accumulation bound. */
 int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n_cb,
                 int V_valid, int V_stride, dec_stream_t stream);
 

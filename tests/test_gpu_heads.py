@@ -51,7 +51,7 @@ def _check_lm_head(B, D, seed):
                                  (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
 @pytest.mark.parametrize("path", ["default", "gemv"])
 def test_lm_head_matches_oracle(B, D, path, monkeypatch):
-    # default: the MFMA kernel from B = 3 on; gemv: the vector-ALU kernel at every B
+    # default: the MFMA kernel at every B; gemv: the vector-ALU kernel at every B
     if path == "gemv":
         monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
     print(f"[lm_head] B={B} D={D} path={path}", flush=True)
