@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdecstep.so")
-SOURCES = ["attn_decode.hip", "sample_topk.hip", "heads.hip", "decstep_abi.hip"]
+SOURCES = ["attn_decode.hip", "sample_topk.hip", "heads.hip", "probe.hip", "decstep_abi.hip"]
 ARCH = "gfx950"
 
 

@@ -7,6 +7,7 @@
 #include "../../include/decstep.h"
 #include "dec_common.h"
 #include "dec_kernels.h"
+#include "probe.h"
 
 namespace {
 
@@ -453,6 +454,20 @@ int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream) {
   if (len == nullptr && step == nullptr) return DEC_E_NULL;
   if (!aligned(len, 4) || !aligned(step, 4)) return DEC_E_ALIGN;
   const hipError_t e = dec::advance_launch(len, step, B, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_probe_read(const void* buf, size_t bytes, uint32_t* sink, dec_stream_t stream) {
+  if (buf == nullptr || sink == nullptr) return DEC_E_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return DEC_E_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return DEC_E_ALIGN;
+  if ((bytes - 1) / (4 * (size_t)dec::kProbeWaveBytes) >= 0x7FFFFFFF) return DEC_E_UNSUPPORTED;
+  const hipError_t e = dec::probe_read_launch(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_probe_empty(dec_stream_t stream) {
+  const hipError_t e = dec::probe_empty_launch(reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 

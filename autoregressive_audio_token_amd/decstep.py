@@ -69,6 +69,8 @@ _SIGS = {
     "dec_lm_head": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dec_embed_sum": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "dec_step_advance": (_I, [_P, _P, _I, _P]),
+    "dec_probe_read": (_I, [_P, _SZ, _P, _P]),
+    "dec_probe_empty": (_I, [_P]),
     "dec_graph_begin": (_I, [_P]),
     "dec_graph_end": (_I, [_P, ctypes.POINTER(_P)]),
     "dec_graph_launch": (_I, [_P, _P]),
@@ -233,6 +235,14 @@ def dec_embed_sum(tokens, E, x, B, n_cb, V_emb, D, stream=None):
 
 def dec_step_advance(len, step, B, stream=None):
     _check(_lib.dec_step_advance(_ptr(len), _ptr(step), B, _stream(stream)))
+
+
+def dec_probe_read(buf, nbytes, sink, stream=None):
+    _check(_lib.dec_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+
+
+def dec_probe_empty(stream=None):
+    _check(_lib.dec_probe_empty(_stream(stream)))
 
 
 def dec_graph_begin(stream):

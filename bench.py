@@ -65,7 +65,208 @@ def parse(argv=None):
                     help="sampler top_k (0: the workload's); above 64 through dec_sample_topk_ex")
     ap.add_argument("--logits-bf16", action="store_true",
                     help="bf16 logits, through dec_sample_topk_ex")
+    ap.add_argument("--schedule", default="stacked", choices=("stacked", "model"),
+                    help="stacked: one attention launch for all layers (self + cross);\n"
+                         "model: per-layer launches, 24 x (self, cross) + the sampler per step")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="a workload with a step count (long_output): the whole generation,\n"
+                         "lengths and steps advanced on the device, timed end to end")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="the calibration kernels: streaming reads at 4 MiB, the workload's\n"
+                         "valid bytes and 4 GiB, and the cost of an empty graph node")
     return ap.parse_args(argv)
+
+
+def read_probe(dec, torch, nbytes, dev, stream, launches, min_pool=1 << 30):
+    """Average launch time (us) of dec_probe_read over nbytes, as a captured graph of
+    `launches` back-to-back launches over rotating buffers (together at least min_pool
+    bytes, so with min_pool above the 256 MB Infinity Cache every launch reads HBM);
+    returns (us, GB/s, buffers)."""
+    sets = max(1, math.ceil(min_pool / nbytes)) if min_pool else 1
+    pool = torch.zeros(sets * nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    bufs = [pool[i * nbytes:(i + 1) * nbytes] for i in range(sets)]
+    n = max(launches, sets)
+    with torch.cuda.stream(stream):
+        for b in bufs:
+            dec.dec_probe_read(b, nbytes, sink, stream)
+        dec.dec_graph_begin(stream)
+        for i in range(n):
+            dec.dec_probe_read(bufs[i % sets], nbytes, sink, stream)
+        g = dec.dec_graph_end(stream)
+        dec.dec_graph_launch(g, stream)
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        dec.dec_graph_launch(g, stream)
+    e1.record(stream)
+    stream.synchronize()
+    dec.dec_graph_destroy(g)
+    us = e0.elapsed_time(e1) * 1e3 / (reps * n)
+    del pool, bufs
+    return us, nbytes / (us * 1e-6) / 1e9, sets
+
+
+def decode_loop(a):
+    """The whole generation of a workload with a step count: step s attends over s + 1 self
+    keys (and the description), samples with Philox uniforms drawn from (seed, step) and
+    the delay mask, then advances the lengths and steps on the device.  Graphs of R steps
+    (one per cache set) are replayed n_steps / R times and timed end to end."""
+    import numpy as np
+    import torch
+    import autoregressive_audio_token_amd as dec
+    from workloads import configs, device as wdev
+
+    w = configs.BY_NAME[a.workload]
+    if w.n_steps <= 1:
+        print(f"--decode-loop needs a workload of several steps; {w.name} is one step",
+              file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    S = w.n_steps
+    B = w.batch
+    c_len = np.full(B, w.cross_len, np.int32)
+    # every row a step can reach is drawn: the self cache up to the last step's length
+    fill = (np.full(B, min(S, w.self_cap)), c_len)
+    log(f"workload {w.name}: staging inputs for {S} steps")
+    d = wdev.step_inputs(w, dev, self_lens=np.ones(B, np.int32), cross_lens=c_len,
+                         fill_lens=fill)
+    R = a.sets if a.sets > 0 else 8
+    if S % R:
+        print(f"--sets must divide the {S} steps", file=sys.stderr)
+        return 2
+    big = ("k_self", "v_self", "k_cross", "v_cross")
+    sets = [{k: d[k] for k in big}]
+    for _ in range(R - 1):
+        sets.append({k: torch.empty_like(d[k]).copy_(d[k]) for k in big})
+    code = dec.DEC_BF16 if w.dtype == "bf16" else dec.DEC_F32
+    nb = dec.dec_attn_workspace_bytes(w.n_layers, B, w.heads, w.head_dim, w.self_cap,
+                                      w.cross_cap)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    o_s = torch.empty((w.n_layers, B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    o_c = torch.empty_like(o_s)
+    tok = torch.empty((B, w.n_codebooks), dtype=torch.int32, device=dev)
+    len_d, step_d = d["len"], d["step"]
+    seed = 0x5EED_0000_0000_0004
+    stream = torch.cuda.Stream(device=dev)
+
+    def step(st, s):
+        dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], len_d, w.self_cap, o_s,
+                          d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
+                          o_c, w.n_layers, B, w.heads, w.head_dim, code, w.scale, ws, nb, s)
+        dec.dec_sample_topk_philox(d["logits"], B, w.n_codebooks, w.vocab_valid, w.vocab_stride,
+                                   d["temperature"], w.top_k, seed, step_d, w.fill_token, tok,
+                                   None, None, s)
+        dec.dec_step_advance(len_d, step_d, B, s)
+
+    def reset():
+        len_d.fill_(1)
+        step_d.fill_(0)
+
+    with torch.cuda.stream(stream):
+        dec.dec_attn_workspace_init(ws, nb, stream)
+        dec.dec_graph_begin(stream)
+        for st in sets:
+            step(st, stream)
+        graph = dec.dec_graph_end(stream)
+        reset()
+        for _ in range(S // R):                 # one untimed generation
+            dec.dec_graph_launch(graph, stream)
+        reset()
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"{R}-step graph captured; timing {S} steps")
+    e0.record(stream)
+    for _ in range(S // R):
+        dec.dec_graph_launch(graph, stream)
+    e1.record(stream)
+    stream.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    dec.dec_graph_destroy(graph)
+    lens_end = len_d.cpu().numpy()
+    steps_end = step_d.cpu().numpy()
+    advanced = bool(np.all(lens_end == 1 + S) and np.all(steps_end == S))
+    out_ok = bool(torch.isfinite(o_s).all().item() and torch.isfinite(o_c).all().item())
+    tok_h = tok.cpu().numpy()
+    tok_ok = bool(np.all(((tok_h >= 0) & (tok_h < w.vocab_valid)) | (tok_h == w.fill_token)))
+    total_bytes = sum(configs.valid_kv_bytes(w, np.full(B, min(s + 1, w.self_cap), np.int32), c_len)
+                      for s in range(S))
+    gbs = total_bytes / (total_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": S,
+        "warmup": S, "ms_per_step": round(total_ms / S, 6),
+        "us_per_step": round(total_ms * 1e3 / S, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_layers": w.n_layers, "batch": B, "heads": w.heads,
+                   "head_dim": w.head_dim, "self_len": f"s + 1 at step s = 0..{S - 1}",
+                   "self_cap": w.self_cap, "cross_len": [int(x) for x in c_len][:4],
+                   "cross_cap": w.cross_cap, "top_k": w.top_k, "cache_sets": R,
+                   "valid_kv_bytes_total": int(total_bytes),
+                   "schedule": f"decode loop: graphs of {R} steps (dec_attn_step + "
+                               f"dec_sample_topk_philox + dec_step_advance, one cache set per "
+                               f"step) replayed {S // R} times; lengths and steps advance on "
+                               f"the device"},
+        "total_ms": round(total_ms, 3),
+        "total_ms_at_70pct_of_peak": round(total_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 3),
+        "roofline": {"bound": "hbm", "kernel": "whole step (attention + sampler + advance)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "checks": {"outputs_finite": out_ok, "tokens_in_range": tok_ok,
+                   "lengths_and_steps_advanced": advanced},
+    }
+    log(f"{S} steps in {total_ms:.3f} ms ({total_ms * 1e3 / S:.2f} us/step)")
+    print(json.dumps(result), flush=True)
+    return 0 if (out_ok and tok_ok and advanced) else 1
+
+
+def calibrate(a):
+    """Streaming-read ceilings and the per-node cost of a captured graph."""
+    import torch
+    import autoregressive_audio_token_amd as dec
+    from workloads import configs, gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+    w = configs.BY_NAME[a.workload]
+    valid = configs.valid_kv_bytes(w, *gen.lengths(w))
+    reads = []
+    for label, nbytes, pool, n in (("4 MiB, one buffer (cache-resident)", 4 << 20, 0, 2000),
+                                   (f"{w.name} valid K/V bytes, rotating buffers", valid,
+                                    1 << 30, 200),
+                                   ("4 GiB, one buffer", 4 << 30, 0, 10)):
+        us, gbs, sets = read_probe(dec, torch, nbytes, dev, stream, n, pool)
+        reads.append({"what": label, "bytes": nbytes, "buffers": sets, "avg_launch_us": round(us, 3),
+                      "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nodes = {}
+    for n in (1, 49):
+        with torch.cuda.stream(stream):
+            dec.dec_graph_begin(stream)
+            for _ in range(n):
+                dec.dec_probe_empty(stream)
+            g = dec.dec_graph_end(stream)
+            dec.dec_graph_launch(g, stream)
+        stream.synchronize()
+        reps = 200
+        e0.record(stream)
+        for _ in range(reps):
+            dec.dec_graph_launch(g, stream)
+        e1.record(stream)
+        stream.synchronize()
+        dec.dec_graph_destroy(g)
+        nodes[n] = e0.elapsed_time(e1) * 1e3 / reps
+    print(json.dumps({"mode": "calibration", "read_kernel": "probe_read_kernel (dec_probe_read)",
+                      "reads": reads, "empty_graph_us": {"1 node": round(nodes[1], 3),
+                                                         "49 nodes": round(nodes[49], 3)},
+                      "us_per_extra_node": round((nodes[49] - nodes[1]) / 48, 3),
+                      "timing": "HIP events around replays of captured graphs"}), flush=True)
+    return 0
 
 
 KERNEL_SOURCES = ("attn_decode.hip", "dec_kernels.h", "dec_common.h")
@@ -260,6 +461,10 @@ def main(argv=None):
         return 2
     if a.copy_mib > 0:
         return copy_calibration(a.copy_mib)
+    if a.calibrate:
+        return calibrate(a)
+    if a.decode_loop:
+        return decode_loop(a)
 
     import numpy as np
     import torch
@@ -278,7 +483,11 @@ def main(argv=None):
     if ex_attn and a.paged:
         print("--cross-mask / --out-bf16 go with the static caches, not --paged", file=sys.stderr)
         return 2
-    plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k)
+    model = a.schedule == "model"
+    if model and (ex_attn or a.paged):
+        print("--schedule model goes with the static caches and fp32 outputs", file=sys.stderr)
+        return 2
+    plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k or model)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s_len, c_len = gen.lengths(w)
@@ -347,6 +556,15 @@ def main(argv=None):
         torch.cuda.synchronize()
 
     def attn(st, s):
+        if model:                        # one self and one cross launch per layer
+            for l in range(w.n_layers):
+                dec.dec_attn_self(d["q_self"][l], st["k_self"][l], st["v_self"][l], d["len"],
+                                  o_s[l], 1, w.batch, w.heads, w.self_cap, w.head_dim, code,
+                                  w.scale, ws, nb, s)
+                dec.dec_attn_cross(d["q_cross"][l], st["k_cross"][l], st["v_cross"][l],
+                                   d["enc_len"], o_c[l], 1, w.batch, w.heads, w.cross_cap,
+                                   w.head_dim, code, w.scale, ws, nb, s)
+            return
         if ex_attn:
             dec.dec_attn_step_ex(d["q_self"], st["k_self"], st["v_self"], d["len"], w.self_cap,
                                  o_s, d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"],
@@ -458,6 +676,8 @@ def main(argv=None):
     pair_us = sum(per) / len(per)
     achieved = valid / (k_us * 1e-6) / 1e9
     dec.dec_graph_destroy(graph)
+    # the measured ceiling: a plain streaming read of the same byte count in one launch
+    probe_us, probe_gbs, probe_sets = read_probe(dec, torch, valid, dev, stream, n_k)
     # the sampler alone: a captured graph of n_k launches
     with torch.cuda.stream(stream):
         dec.dec_graph_begin(stream)
@@ -476,8 +696,12 @@ def main(argv=None):
     traffic_rec, traffic_why = counter_traffic(w.name)
     if not plain:
         traffic_rec, traffic_why = None, "counters describe the default configuration only"
-    attn_entry = ("dec_attn_step_ex" if ex_attn else
+    if model:
+        traffic_rec, traffic_why = None, "counters describe the stacked launch only"
+    attn_entry = ("dec_attn_self + dec_attn_cross per layer" if model else
+                  "dec_attn_step_ex" if ex_attn else
                   "dec_attn_step_paged" if a.paged else "dec_attn_step")
+    attn_launches = 2 * w.n_layers if model else 1
     samp_entry = "dec_sample_topk_ex" if ex_samp else "dec_sample_topk"
 
     result = {
@@ -504,8 +728,10 @@ def main(argv=None):
             "static_cache_bytes_per_set": static_bytes,
             "kv_layout": (f"self cache paged, {a.paged} keys per block" if a.paged
                           else "static caches"),
-            "schedule": f"hipGraph of R steps; step = {attn_entry} (self+cross, all layers, "
-                        f"one launch) + {samp_entry}",
+            "schedule": (f"model-shaped: hipGraph of R steps; step = {attn_entry} "
+                         f"({attn_launches} launches) + {samp_entry}" if model else
+                         f"hipGraph of R steps; step = {attn_entry} (self+cross, all layers, "
+                         f"one launch) + {samp_entry}"),
             "variant": {"head_dim": w.head_dim, "cross_mask": mask_note,
                         "attention_outputs": "bf16" if a.out_bf16 else "f32",
                         "logits": "bf16" if a.logits_bf16 else "f32", "top_k": top_k},
@@ -513,6 +739,7 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm",
             "kernel": f"attn_decode_kernel ({attn_entry})",
+            "launches_per_step": attn_launches,
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_rec["hbm_bytes_per_launch"] if traffic_rec else None,
@@ -520,11 +747,20 @@ def main(argv=None):
                 "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch", "fetch_scale",
                 "write_scale", "ratio_to_algorithmic")} if traffic_rec else {})},
             "avg_launch_us": round(k_us, 3),
-            "avg_launch_us_method": f"HIP events around a captured graph of {n_k} launches, "
-                                    f"{k_reps} replays",
+            "avg_launch_us_method": (f"HIP events around a captured graph of {n_k} attention "
+                                     f"steps ({attn_launches} launches each), {k_reps} replays"
+                                     if model else
+                                     f"HIP events around a captured graph of {n_k} launches, "
+                                     f"{k_reps} replays"),
             "event_pair_avg_us": round(pair_us, 3),
             "event_pair_median_us": round(per[len(per) // 2], 3), "launches": n_k,
             "algorithmic_bytes_per_launch": valid,
+            "measured_read_gbs": round(probe_gbs, 1),
+            "frac_of_measured": round(achieved / probe_gbs, 4),
+            "measured_read_method": f"dec_probe_read (a plain streaming read) over the same "
+                                    f"{valid} bytes in one launch: a captured graph of "
+                                    f"{max(n_k, probe_sets)} launches over {probe_sets} rotating "
+                                    f"buffers, {probe_us:.3f} us per launch",
         },
         "sampler": {"kernel": f"sample_topk_kernel ({samp_entry})", "top_k": top_k,
                     "avg_launch_us": round(samp_us, 3),

@@ -291,6 +291,21 @@ int dec_embed_sum(const int32_t* tokens, const void* E, float* x, int B, int n_c
  * len[b] += 1 (if len != NULL) and step[b] += 1 (if step != NULL) for b < B. */
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);
 
+/* Calibration for the measurements; neither is a step of a decode step.
+ * dec_probe_read streams [buf, buf + bytes) once (16-byte non-temporal loads,
+ * 8 KiB per wavefront, one workgroup of four wavefronts per 32 KiB), giving
+ * the HBM read bandwidth this part reaches for that byte count in one launch:
+ * the ceiling an attention launch of the same bytes is compared against,
+ * beside the specification peak.  A lane whose 32 words XOR to 0x9E3779B9
+ * stores its global lane index (wavefront * 64 + lane, where wavefront w reads
+ * bytes [8192 w, 8192 w + 8192) and lane l of it the 16 bytes at 16 l + 1024 u,
+ * u = 0..7) to sink[0]; nothing else is written.  buf 16-byte aligned, bytes a
+ * positive multiple of 16 (else DEC_E_ALIGN / DEC_E_SHAPE); device pointers,
+ * caller-owned.  dec_probe_empty launches one wavefront that does nothing: the
+ * fixed cost of one node of a captured graph. */
+int dec_probe_read(const void* buf, size_t bytes, uint32_t* sink, dec_stream_t stream);
+int dec_probe_empty(dec_stream_t stream);
+
 /* Graph capture of a whole decode step ("Analysis and improvements": the step
  * is captured once and replayed with a single launch).  begin/end bracket
  * ordinary dec_* calls on a non-default stream; end returns an executable

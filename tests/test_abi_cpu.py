@@ -293,6 +293,13 @@ def test_misc_validation():
     assert D.raw_status("dec_attn_workspace_init", None, 0, None) == D.DEC_OK
     assert D.raw_status("dec_attn_workspace_init", None, 64, None) == D.DEC_E_NULL
     assert D.raw_status("dec_attn_workspace_init", A + 4, 64, None) == D.DEC_E_ALIGN
+    # the calibration read: pointers, a positive multiple of 16 bytes, alignment
+    assert D.raw_status("dec_probe_read", None, 16, A, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_probe_read", A, 16, None, None) == D.DEC_E_NULL
+    assert D.raw_status("dec_probe_read", A, 0, A, None) == D.DEC_E_SHAPE
+    assert D.raw_status("dec_probe_read", A, 24, A, None) == D.DEC_E_SHAPE
+    assert D.raw_status("dec_probe_read", A + 4, 16, A, None) == D.DEC_E_ALIGN
+    assert D.raw_status("dec_probe_read", A, 16, A + 2, None) == D.DEC_E_ALIGN
 
 
 def test_order_key_map_is_monotone_over_all_float32_bit_patterns():

@@ -55,3 +55,18 @@ def test_variant_options_parse():
                      "--out-bf16", "--top-k", "250", "--logits-bf16"])
     assert (a.head_dim, a.cross_mask, a.mask_runs, a.out_bf16, a.top_k, a.logits_bf16) == \
         (128, 0.3, 64, True, 250, True)
+
+
+def test_model_schedule_with_widened_or_paged_attention_is_refused():
+    assert bench.main(["--schedule", "model", "--paged", "64"]) == 2
+    assert bench.main(["--schedule", "model", "--out-bf16"]) == 2
+
+
+def test_decode_loop_needs_a_workload_with_steps():
+    assert bench.main(["--decode-loop", "--workload", "long_description"]) == 2
+
+
+def test_measurement_options_parse():
+    a = bench.parse(["--schedule", "model", "--decode-loop", "--calibrate"])
+    assert (a.schedule, a.decode_loop, a.calibrate) == ("model", True, True)
+    assert bench.parse([]).schedule == "stacked"
