@@ -7,7 +7,8 @@
 // bytes plus a few hundred bytes per sequence.
 //
 // Split-K flash-decode, arranged for CDNA4:
-//   * A sequence of n valid keys is cut into chunks of kAttnChunk keys.  A
+//   * A sequence of n valid keys is cut into chunks of 1024 keys (a launch with
+//     too few chunks to give every CU one cuts them smaller, down to 128).  A
 //     workgroup of kAttnWaves wavefronts streams a chunk in tile rounds: in
 //     each round every wave reads a 32-key tile (a key row of 64 bf16 is 128 B
 //     = 8 lanes x 16 B, so one dwordx4 load instruction covers 8 consecutive
@@ -144,11 +145,14 @@ __device__ __forceinline__ void accum_slice(float (&acc)[EPL], float p, const u3
   for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, x[e], acc[e]);
 }
 
-__device__ __forceinline__ int nchunks(int n) { return n > 0 ? (n + kAttnChunk - 1) / kAttnChunk : 0; }
+// Chunks of 1 << clog keys covering n keys.
+__device__ __forceinline__ int nchunks(int n, int clog) {
+  return n > 0 ? ((n - 1) >> clog) + 1 : 0;
+}
 
 // Work items per (layer, head) of a sequence with n valid keys.
-__device__ __forceinline__ int items_per_lh(int n, int cpi) {
-  const int c = nchunks(n);
+__device__ __forceinline__ int items_per_lh(int n, int cpi, int clog) {
+  const int c = nchunks(n, clog);
   return c > cpi ? (c + cpi - 1) / cpi : 1;
 }
 
@@ -165,13 +169,13 @@ __device__ __forceinline__ int waves_per_seq(int n) {
 
 // Work items of a (segment, b) group with n valid keys.
 template <int HD>
-__device__ __forceinline__ int group_items(int n, int NLH, int cpi) {
+__device__ __forceinline__ int group_items(int n, int NLH, int cpi, int clog) {
   const int S = waves_per_seq<HD>(n);
   if (S < kAttnWaves) {
     const int P = kAttnWaves / S;
     return (NLH + P - 1) / P;
   }
-  return NLH * items_per_lh(n, cpi);
+  return NLH * items_per_lh(n, cpi, clog);
 }
 
 // Fold chunk state (mc, lc, ac) into the running state (m, l, a); the first
@@ -291,7 +295,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   constexpr int EPL = TileT::EPL;
   constexpr int LPK = TileT::LPK;
   constexpr int KPT = TileT::KPT;
-  constexpr int TPC = attn_tiles_per_chunk(HD);
   constexpr int PS = attn_part_stride(HD);
   static_assert(kAttnThreads % HD == 0, "whole sequences per combining pass");
   static_assert(!EX || KPT == 16 || KPT == 32 || KPT == 64, "a tile's mask bits lie in whole words");
@@ -313,6 +316,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   const int G = p.nseg * B;
   const int NLH = p.NL * p.H;
   const int cpi = p.cpi;
+  const int clog = p.chunk_log2;  // keys per chunk: 1 << clog, whole tile rounds
   int* s_n = s_dyn;
   int* s_order = s_dyn + G;
   int* s_pref = s_dyn + 2 * G;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
       n = len[cross ? lane - B : lane];
       n = n < 0 ? 0 : (n > cap ? cap : n);
-      items = group_items<HD>(n, NLH, cpi);
+      items = group_items<HD>(n, NLH, cpi, clog);
     }
     int rank = 0;  // stable rank by descending length
     for (int j = 0; j < G; ++j) {
@@ -371,7 +375,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const int lo = min(G, tid * per);
     const int hi = min(G, lo + per);
     int local = 0;
-    for (int i = lo; i < hi; ++i) local += group_items<HD>(s_n[s_order[i]], NLH, cpi);
+    for (int i = lo; i < hi; ++i) local += group_items<HD>(s_n[s_order[i]], NLH, cpi, clog);
     int ex = wave_inclusive_sum_int(local, lane) - local;
     if (lane == kWave - 1) s_wsum[wave] = ex + local;
     __syncthreads();
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     }
     for (int i = lo; i < hi; ++i) {
       s_pref[i] = ex;
-      ex += group_items<HD>(s_n[s_order[i]], NLH, cpi);
+      ex += group_items<HD>(s_n[s_order[i]], NLH, cpi, clog);
     }
     if (tid == 0) s_pref[G] = total;
     __syncthreads();
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const bool cross = g >= B;
     const AttnSeg& S = cross ? p.seg[1] : p.seg[0];
     const int b = cross ? g - B : g;
-    const int nck = nchunks(n);
+    const int nck = nchunks(n, clog);
     const int spw = waves_per_seq<HD>(n);        // waves per sequence
     const bool packed = spw < kAttnWaves;        // several sequences share this item
     const int P = kAttnWaves / spw;              // sequences in this item (packed)
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       c1 = nck;
       whole = true;
     } else {
-      const int ipl = items_per_lh(n, cpi);
+      const int ipl = items_per_lh(n, cpi, clog);
       const int k = r % ipl;
       wave_lh = r / ipl;
       wave_part = wave;
@@ -456,6 +460,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     }
 
     constexpr int kStep = kAttnWaves * KPT;  // keys between a wave's tiles
+    const int tpc = (1 << clog) / kStep;     // a wave's tiles per chunk
     constexpr int kRowBytes = HD * (int)sizeof(T);
     const int lane_off = kg * kRowBytes + dl * 16;
     const bool paged = PAGED && S.table != nullptr;  // uniform: per segment
@@ -479,13 +484,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
 
     for (int c = c0; c < c1; ++c) {
       // tile t of this wave starts at key cb + t * kStep; packed items read one tile
-      const int cb = c * kAttnChunk + wave_part * KPT;
+      const int cb = (c << clog) + wave_part * KPT;
       float m_g = -INFINITY, l_g = 0.f;  // this lane group's online state
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
       if (wave_ok && cb < n) {  // uniform across the wave
-        const int nt = packed ? 1 : min(TPC, (n - cb + kStep - 1) / kStep);
+        const int nt = packed ? 1 : min(tpc, (n - cb + kStep - 1) / kStep);
         // paged: lane i < nt holds the physical block of the wave's tile i in this chunk
         int blk_of = 0;
         if (paged && lane < nt)
@@ -602,13 +607,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     __syncthreads();
     if (s_last) {
       if (slot_ok) {
+        // the states of up to 8 chunks are in flight at once (a load past the last chunk
+        // re-reads it and is not folded), then folded in chunk order
+        constexpr int kFoldBatch = 8;
         const float* pp = S.part + slot_sidx * S.nck_cap * PS;
-        for (int cc = 0; cc < nck; ++cc) {
-          const float* q = pp + cc * PS;
-          const float mc = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const float lc = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const float ac = __hip_atomic_load(q + 4 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          fold_chunk<EX>(cc == 0, mc, lc, ac, fm, fl, fa);
+        for (int cf = 0; cf < nck; cf += kFoldBatch) {
+          float mc[kFoldBatch], lc[kFoldBatch], ac[kFoldBatch];
+#pragma unroll
+          for (int j = 0; j < kFoldBatch; ++j) {
+            const float* q = pp + min(cf + j, nck - 1) * PS;
+            mc[j] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lc[j] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ac[j] = __hip_atomic_load(q + 4 + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int j = 0; j < kFoldBatch; ++j)
+            if (cf + j < nck) fold_chunk<EX>(cf + j == 0, mc[j], lc[j], ac[j], fm, fl, fa);
         }
         store_out<EX>(S, slot_sidx * HD + d, fa, fl);
       }
@@ -660,7 +674,15 @@ void attn_kernel_go(int variant, int blocks, size_t lds, hipStream_t stream, con
 }
 }  // namespace
 
-hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t stream) {
+// Work items of a launch at chunk 1 << clog, every sequence at full capacity.
+static long long items_at(const AttnParams& p, int clog) {
+  AttnParams q = p;
+  for (int s = 0; s < q.nseg; ++s) q.seg[s].nck_cap = ((q.seg[s].L_cap - 1) >> clog) + 1;
+  return attn_items_cap(q);
+}
+
+hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_t stream) {
+  AttnParams p = p_in;
   const int G = p.nseg * p.B;
   const size_t lds = (size_t)(3 * G + 1) * sizeof(int);
   const bool paged = p.seg[0].table != nullptr || (p.nseg > 1 && p.seg[1].table != nullptr);
@@ -673,17 +695,34 @@ hipError_t attn_launch(const AttnParams& p, int dtype, int blocks, hipStream_t s
                                 : attn_kernel_ptr<uint16_t, kAttnHeadDim>(variant))
                         : (wide ? attn_kernel_ptr<float, kAttnHeadDimWide>(variant)
                                 : attn_kernel_ptr<float, kAttnHeadDim>(variant));
-  if (blocks <= 0) {
-    int dev = 0;
+  const bool choose_chunk = p.chunk_log2 == 0;
+  int dev = 0, cus = 0;
+  if (blocks <= 0 || choose_chunk) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     DevInfo& di = g_dev[dev & 63];
-    int cus = di.cus.load(std::memory_order_relaxed);
+    cus = di.cus.load(std::memory_order_relaxed);
     if (cus == 0) {
       e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
       di.cus.store(cus, std::memory_order_relaxed);
     }
+  }
+  if (choose_chunk) {
+    // 1024-key chunks; a split launch with fewer items than a quarter of the CUs halves
+    // them (down to the smallest chunk the workspace holds partials for), so more CUs
+    // share its bytes.  Measured on 16 sequences of 1024 keys: 64 items of 256 keys beat
+    // 128 of 128 (each item pays a prologue and a fold) and 16 or 32 larger ones.
+    p.chunk_log2 = attn_log2(kAttnChunk);
+    if (p.cpi == 1)
+      while (p.chunk_log2 > p.min_chunk_log2 && items_at(p, p.chunk_log2) * 4 < cus)
+        --p.chunk_log2;
+  }
+  for (int s = 0; s < 2; ++s)
+    p.seg[s].nck_cap = p.seg[s].L_cap > 0 ? ((p.seg[s].L_cap - 1) >> p.chunk_log2) + 1 : 0;
+  if (blocks <= 0) {
+    hipError_t e = hipSuccess;
+    DevInfo& di = g_dev[dev & 63];
     int occ = di.occ[dtype][wide][variant].load(std::memory_order_relaxed);
     if (occ == 0 || G > 64) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);

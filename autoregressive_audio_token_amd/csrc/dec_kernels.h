@@ -24,7 +24,7 @@ static_assert(kAttnKeysPerTile <= kAttnMinBlockKeys, "a tile never crosses a pag
 #ifndef DEC_ATTN_CHUNK
 #define DEC_ATTN_CHUNK 1024
 #endif
-constexpr int kAttnChunk = DEC_ATTN_CHUNK;          // keys per chunk
+constexpr int kAttnChunk = DEC_ATTN_CHUNK;          // keys per chunk (the largest chunk)
 constexpr int kAttnHeadDim = 64;                   // the model's head dim; 128 is also built
 constexpr int kAttnHeadDimWide = 128;
 // keys per tile and tiles per chunk at head dim HD
@@ -35,6 +35,14 @@ static_assert(attn_tiles_per_chunk(kAttnHeadDim) * kAttnWaves * kAttnKeysPerTile
 static_assert(attn_tiles_per_chunk(kAttnHeadDimWide) * kAttnWaves *
                       attn_keys_per_tile(kAttnHeadDimWide) == kAttnChunk,
               "a chunk is a whole number of workgroup tile rounds");
+// Launches with few sequences may cut chunks smaller, down to this many keys, so that
+// every CU gets a work item; a power of two and a whole number of tile rounds.
+constexpr int kAttnMinChunk = kAttnWaves * kAttnKeysPerTile > 128 ? kAttnWaves * kAttnKeysPerTile : 128;
+static_assert((kAttnMinChunk & (kAttnMinChunk - 1)) == 0 && kAttnMinChunk <= kAttnChunk &&
+                  kAttnMinChunk % (kAttnWaves * kAttnKeysPerTile) == 0 &&
+                  kAttnMinChunk % (kAttnWaves * attn_keys_per_tile(kAttnHeadDimWide)) == 0,
+              "the smallest chunk is a whole number of workgroup tile rounds");
+constexpr int attn_log2(int x) { return x <= 1 ? 0 : 1 + attn_log2(x / 2); }
 // floats per chunk partial: m, l, pad, pad, acc[hd]
 constexpr int attn_part_stride(int hd) { return 4 + hd; }
 constexpr int kAttnMaxGroups = 4096;                // (segments x batch) handled per launch
@@ -52,7 +60,7 @@ struct AttnSeg {
   float* part;            // [NL*B*H, nck_cap, attn_part_stride(hd)] chunk partials (split mode)
   int32_t* ticket;        // [NL*B*H] chunk arrival counters (split mode), zero between calls
   int L_cap;              // keys a sequence can hold (paged: table_stride << bs_log2)
-  int nck_cap;            // ceil(L_cap / kAttnChunk)
+  int nck_cap;            // ceil(L_cap / chunk), the chunk of this launch
   // paged cache (table != nullptr): k, v are pools [NL, n_blocks, H, 1 << bs_log2, hd]
   const int32_t* table;   // [B, table_stride] physical block of each logical block
   int table_stride;
@@ -70,6 +78,8 @@ struct AttnParams {
   int NL, B, H;
   int hd;                 // 64 or 128 (selects the instantiation)
   int cpi;                // chunks per work item (>= nck_cap of every segment: no split)
+  int chunk_log2;         // log2(keys per chunk); 0: the launcher chooses
+  int min_chunk_log2;     // the smallest chunk the workspace holds partials for
   float qscale;           // scale * log2(e): scores are formed in base 2
 };
 

@@ -22,24 +22,36 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Workspace of one attention segment, used when a launch spreads the chunks of a
-// sequence over several workgroups: per-sequence arrival tickets (zero between
-// calls), then the chunk states.  Capacities that fit one chunk need none.
-struct SegLayout {
-  size_t ticket_off = 0, part_off = 0, bytes = 0;
-  int nck_cap = 0;
+// Workspace of an attention call, used when a launch spreads the chunks of a sequence
+// over several workgroups: two regions of per-sequence arrival tickets (the call's first
+// segment, then its second; zero between calls), then each segment's chunk states at
+// `chunk` keys per chunk.  The tickets sit at the same places whatever chunk a call
+// uses, so the chunk states of one call never land on another's tickets.  Capacities
+// that fit one chunk need none.
+struct WsLayout {
+  size_t ticket_bytes = 0;  // one ticket region
+  size_t part_off[2] = {0, 0};
+  size_t bytes = 0;
 };
 
-SegLayout seg_layout(int NL, int B, int H, int L_cap, int hd) {
-  SegLayout s;
-  if (L_cap <= 0) return s;
-  s.nck_cap = (L_cap + dec::kAttnChunk - 1) / dec::kAttnChunk;
-  if (s.nck_cap <= 1) return s;
+WsLayout ws_layout(int NL, int B, int H, int hd, const int (&L_cap)[2], int chunk) {
+  WsLayout w;
+  int nck[2];
+  bool any = false;
+  for (int s = 0; s < 2; ++s) {
+    nck[s] = L_cap[s] > 0 ? (L_cap[s] + chunk - 1) / chunk : 0;
+    any = any || nck[s] > 1;
+  }
+  if (!any) return w;
   const size_t nseq = (size_t)NL * B * H;
-  s.ticket_off = 0;
-  s.part_off = align_up(nseq * sizeof(int32_t), 256);
-  s.bytes = s.part_off + align_up(nseq * s.nck_cap * dec::attn_part_stride(hd) * sizeof(float), 256);
-  return s;
+  w.ticket_bytes = align_up(nseq * sizeof(int32_t), 256);
+  size_t off = 2 * w.ticket_bytes;
+  for (int s = 0; s < 2; ++s) {
+    w.part_off[s] = off;
+    if (nck[s] > 1) off += align_up(nseq * nck[s] * dec::attn_part_stride(hd) * sizeof(float), 256);
+  }
+  w.bytes = off;
+  return w;
 }
 
 bool hd_ok(int hd) { return hd == dec::kAttnHeadDim || hd == dec::kAttnHeadDimWide; }
@@ -118,16 +130,26 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
       if (!aligned(segs[s].mask, 8)) return DEC_E_ALIGN;
     }
   }
-  size_t need = 0;
-  SegLayout lay[2];
-  for (int s = 0; s < nseg; ++s) {
-    lay[s] = seg_layout(NL, B, H, segs[s].L_cap, hd);
-    need += lay[s].bytes;
-  }
-  if (need > 0) {
+  // required: the chunk states at 1024-key chunks; a workspace that also holds them at
+  // the smallest chunk lets a launch with few sequences cut its chunks smaller
+  const int caps[2] = {segs[0].L_cap, nseg > 1 ? segs[1].L_cap : 0};
+  const WsLayout lay_max = ws_layout(NL, B, H, hd, caps, dec::kAttnChunk);
+  const WsLayout lay_min = ws_layout(NL, B, H, hd, caps, dec::kAttnMinChunk);
+  if (lay_max.bytes > 0) {
     if (ws == nullptr) return DEC_E_NULL;
     if (!aligned(ws, 16)) return DEC_E_ALIGN;
-    if (ws_bytes < need) return DEC_E_WORKSPACE;
+    if (ws_bytes < lay_max.bytes) return DEC_E_WORKSPACE;
+  }
+  const bool small_ok =
+      lay_min.bytes > 0 && ws != nullptr && aligned(ws, 16) && ws_bytes >= lay_min.bytes;
+  const WsLayout& lay = small_ok ? lay_min : lay_max;
+  const int min_log2 = dec::attn_log2(small_ok ? dec::kAttnMinChunk : dec::kAttnChunk);
+  int chunk_log2 = 0;  // the launcher chooses
+  const int chunk_env = env_int("DECSTEP_ATTN_CHUNK", 0);
+  if (chunk_env != 0) {  // a fixed chunk (tests of every cut)
+    if (!is_pow2(chunk_env) || chunk_env > dec::kAttnChunk || chunk_env < (1 << min_log2))
+      return DEC_E_UNSUPPORTED;
+    chunk_log2 = dec::attn_log2(chunk_env);
   }
 
   dec::AttnParams p{};
@@ -137,8 +159,8 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   p.H = H;
   p.hd = hd;
   p.qscale = scale * 1.4426950408889634f;  // log2(e)
-  int nck_max = 1;
-  size_t off = 0;
+  p.chunk_log2 = chunk_log2;
+  p.min_chunk_log2 = min_log2;
   for (int s = 0; s < nseg; ++s) {
     dec::AttnSeg& g = p.seg[s];
     g.q = segs[s].q;
@@ -147,7 +169,6 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.len = segs[s].len;
     g.out = segs[s].out;
     g.L_cap = segs[s].L_cap;
-    g.nck_cap = lay[s].nck_cap;
     g.table = segs[s].table;
     g.table_stride = segs[s].table_stride;
     g.n_blocks = segs[s].n_blocks;
@@ -155,19 +176,17 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.mask = segs[s].mask;
     g.mask_words = segs[s].mask_words;
     g.out_bf16 = segs[s].out_bf16;
-    if (lay[s].bytes > 0) {
-      char* base = static_cast<char*>(ws) + off;
-      g.ticket = reinterpret_cast<int32_t*>(base + lay[s].ticket_off);
-      g.part = reinterpret_cast<float*>(base + lay[s].part_off);
+    if (lay.bytes > 0) {  // nck_cap follows the chunk the launcher settles on
+      char* base = static_cast<char*>(ws);
+      g.ticket = reinterpret_cast<int32_t*>(base + s * lay.ticket_bytes);
+      g.part = reinterpret_cast<float*>(base + lay.part_off[s]);
     }
-    off += lay[s].bytes;
-    if (lay[s].nck_cap > nck_max) nck_max = lay[s].nck_cap;
   }
   // Few sequences: every chunk is its own work item, so the CUs get equal bytes;
   // otherwise one workgroup owns a whole sequence (no cross-workgroup traffic).
   const long long seqs = (long long)NL * B * H * nseg;
   const int split = env_int("DECSTEP_ATTN_SPLIT", seqs < dec::kAttnSplitBelow ? 1 : 0);
-  p.cpi = split ? 1 : nck_max;
+  p.cpi = split ? 1 : (1 << 24);  // whole mode: every chunk of a sequence in one item
   if (nseg == 1) p.seg[1] = p.seg[0];
   const hipError_t e = dec::attn_launch(p, dtype, env_int("DECSTEP_ATTN_BLOCKS", 0), stream);
   return e == hipSuccess ? DEC_OK : hip_fail(e);
@@ -183,8 +202,8 @@ size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_se
                                 int L_cap_cross) {
   if (!hd_ok(hd) || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 0 || L_cap_cross < 0)
     return 0;
-  return seg_layout(n_layers, B, H, L_cap_self, hd).bytes +
-         seg_layout(n_layers, B, H, L_cap_cross, hd).bytes;
+  const int caps[2] = {L_cap_self, L_cap_cross};
+  return ws_layout(n_layers, B, H, hd, caps, dec::kAttnMinChunk).bytes;
 }
 
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {

@@ -55,20 +55,31 @@ enum dec_status {
   DEC_E_ALIGN = 7         /* a pointer is not aligned as required */
 };
 
-/* Keys per split-K chunk of the attention kernels.  A sequence of n valid
- * keys is cut into ceil(n / chunk) chunks; each chunk's partial softmax state
- * (max, sum, weighted values) is formed in a fixed order and the chunk states
- * fold in chunk order.  The cut depends on n only, never on the grid or on how
- * chunks are spread over workgroups, so results are bitwise reproducible. */
+/* Keys per split-K chunk of the attention kernels: the largest chunk, 1024.
+ * A sequence of n valid keys is cut into ceil(n / chunk) chunks; each chunk's
+ * partial softmax state (max, sum, weighted values) is formed in a fixed order
+ * and the chunk states fold in chunk order.  A launch with few sequences,
+ * whose chunks (counted at full capacity) would give fewer than one work item
+ * per four CUs, halves the chunk (down to 128 keys) until they do, when its
+ * workspace holds the chunk states at 128 keys (dec_attn_workspace_bytes
+ * sizes it so).  The cut therefore depends
+ * on n, the call's shape and capacities, the workspace size and the device's
+ * CU count, never on the grid or on how chunks are spread over workgroups:
+ * results are bitwise reproducible for a given call on a given device. */
 int dec_attn_chunk_keys(void);
 
 /* Workspace bytes for attention over n_layers x B x H sequences with a self
  * cache of L_cap_self slots and a cross cache of L_cap_cross slots (pass 0 for
- * a cache that the call does not use).  It holds, per sequence, an arrival
- * counter and the chunk states used when a launch spreads a sequence's chunks
- * over several workgroups (launches with few sequences do); capacities that fit
- * one chunk need none.  One workspace sized for both caches serves
- * dec_attn_self, dec_attn_cross and dec_attn_step.  Returns 0 on bad sizes. */
+ * a cache that the call does not use).  It holds two regions of per-sequence
+ * arrival counters (a call's first and second cache) and the chunk states used
+ * when a launch spreads a sequence's chunks over several workgroups (launches
+ * with few sequences do), sized for 128-key chunks; capacities of at most 128
+ * slots need none.  A call also accepts a smaller workspace that holds the
+ * states at 1024-key chunks (none when its capacities fit 1024 slots), and
+ * then keeps 1024-key chunks.  One workspace sized for both caches serves
+ * dec_attn_self, dec_attn_cross and dec_attn_step of one n_layers x B x H
+ * shape; calls of another shape need their own workspace, or
+ * dec_attn_workspace_init in between.  Returns 0 on bad sizes. */
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,
                                 int L_cap_self, int L_cap_cross);
 

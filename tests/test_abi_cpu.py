@@ -84,12 +84,13 @@ def test_attention_host_validation():
     assert _attn(L=1 << 22, hd=128, dt=1) == D.DEC_E_UNSUPPORTED   # 2 GiB per sequence
     assert _attn(q=A + 8) == D.DEC_E_ALIGN
     assert _attn(out=A + 2) == D.DEC_E_ALIGN
-    # a cache longer than one chunk needs the workspace
+    # a cache longer than one chunk needs the workspace: at least the states at 1024-key
+    # chunks (two 256-byte ticket regions, 4 chunk states of 68 floats rounded to 1280 B)
     L = 4 * dec.dec_attn_chunk_keys()
     need = dec.dec_attn_workspace_bytes(1, 1, 1, 64, L, 0)
-    assert need > 0
+    assert need == 512 + 32 * 68 * 4
     assert _attn(L=L, ws=None, wsb=0) == D.DEC_E_NULL
-    assert _attn(L=L, ws=A, wsb=need - 1) == D.DEC_E_WORKSPACE
+    assert _attn(L=L, ws=A, wsb=512 + 1280 - 1) == D.DEC_E_WORKSPACE
     assert _attn(L=L, ws=A + 4, wsb=need) == D.DEC_E_ALIGN
 
 
@@ -98,21 +99,48 @@ def test_step_validation_and_workspace_sizes():
     st = D.raw_status("dec_attn_step", A, A, A, A, 4096, A, A, A, A, None, 64, A,
                       24, 1, 16, 64, 0, ctypes.c_float(0.125), A, 16, None)
     assert st == D.DEC_E_NULL
-    need = dec.dec_attn_workspace_bytes(24, 1, 16, 64, 4096, 1024)
+    # required: the states at 1024-key chunks, two ticket regions of 384 sequences
+    # (1536 B each) and 4 self chunks of 68 floats per sequence (the cross cache fits one)
+    req = 2 * 1536 + 384 * 4 * 68 * 4
+    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 4096, 1024) > req
     st = D.raw_status("dec_attn_step", A, A, A, A, 4096, A, A, A, A, A, 1024, A,
-                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, need - 1, None)
+                      24, 1, 16, 64, 0, ctypes.c_float(0.125), A, req - 1, None)
     assert st == D.DEC_E_WORKSPACE
     ck = dec.dec_attn_chunk_keys()
-    # one chunk of capacity: no workspace at all
-    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, ck, ck) == 0
+    assert ck == 1024
+    # capacities within the smallest chunk (128 keys): no workspace at all
+    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 128, 128) == 0
+    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 129, 0) > 0
+    # two ticket regions of 24 sequences (256 bytes each), then the chunk states at
+    # 128-key chunks: 80 chunks of the self cache and 24 of the cross cache, 68 floats each
     s = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 0)
     c = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 0, 3 * ck)
-    assert dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 3 * ck) == s + c
-    assert s >= 24 * 10 * 68 * 4 and c >= 24 * 3 * 68 * 4
+    both = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 3 * ck)
+    assert s == 512 + 24 * 80 * 68 * 4 and c == 512 + 24 * 24 * 68 * 4
+    assert both == s + c - 512
     assert dec.dec_attn_workspace_bytes(2, 3, 4, 32, 10, 10) == 0
     # head dim 128: chunk states of 4 + 128 floats
     w128 = dec.dec_attn_workspace_bytes(2, 3, 4, 128, 10 * ck, 0)
-    assert w128 >= 24 * 10 * 132 * 4 and w128 > s
+    assert w128 == 512 + 24 * 80 * 132 * 4
+
+
+
+@_no_gpu
+def test_workspace_down_to_the_1024_key_states(monkeypatch):
+    # An invalid fixed chunk is refused right after the workspace check, so these calls
+    # show which workspaces pass that check without launching anything.
+    def self_call(L_cap, ws, nbytes):
+        return D.raw_status("dec_attn_self", A, A, A, A, A, 2, 3, 4, L_cap, 64, 0,
+                            ctypes.c_float(0.125), ws, nbytes, None)
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "3")
+    assert self_call(1024, None, 0) == D.DEC_E_UNSUPPORTED      # one 1024-key chunk: none
+    small = 512 + 24 * 4 * 68 * 4                                 # 4 chunks at 1024 keys
+    assert self_call(4096, A, small - 1) == D.DEC_E_WORKSPACE
+    assert self_call(4096, A, small) == D.DEC_E_UNSUPPORTED
+    # a fixed chunk below what the workspace holds states for is refused
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "128")
+    assert self_call(4096, A, small) == D.DEC_E_UNSUPPORTED
+    assert self_call(1024, None, 0) == D.DEC_E_UNSUPPORTED
 
 
 def _samp(**kw):
@@ -158,8 +186,9 @@ def test_paged_attention_host_validation():
     assert _paged(tab=A + 2) == D.DEC_E_ALIGN
     assert _paged(k=A + 8) == D.DEC_E_ALIGN
     need = dec.dec_attn_workspace_bytes(24, 1, 16, 64, 64 * 64, 0)
-    assert need > 0
-    assert _paged(wsb=need - 1) == D.DEC_E_WORKSPACE
+    req = 2 * 1536 + 384 * 4 * 68 * 4       # the states at 1024-key chunks (4096 keys)
+    assert need > req
+    assert _paged(wsb=req - 1) == D.DEC_E_WORKSPACE
     assert _paged(ws=None) == D.DEC_E_NULL
     st = D.raw_status("dec_attn_step_paged", A, A, A, None, A, 64, 100, 64, A, A, A, A, A, 64, A,
                       24, 1, 16, 64, 0, ctypes.c_float(0.125), A, 1 << 30, None)

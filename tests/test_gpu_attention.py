@@ -183,12 +183,14 @@ def test_fp32_tiny_with_invalid_slots_poisoned_by_inf():
     _check("self", w, d, hp.attn("self", w, d), src, all_rows(w), d["self_len_host"])
 
 
+@pytest.mark.parametrize("chunk", [128, 256, 512, 1024])
 @pytest.mark.parametrize("n", [700, 1024, 1025, 3000, 4096])
-def test_split_and_whole_sequence_modes_agree_bitwise(n, monkeypatch):
-    # chunks spread over workgroups (folded by the combine kernel) versus one
-    # workgroup per sequence: identical arithmetic, identical bits
+def test_split_and_whole_sequence_modes_agree_bitwise(n, chunk, monkeypatch):
+    # chunks spread over workgroups (folded by the last one to arrive) versus one
+    # workgroup per sequence, at the same chunk: identical arithmetic, identical bits
     w = configs.MINI_V1
     d = _inputs(w, self_lens=[n])
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", str(chunk))
     monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "0")
     whole = hp.host(hp.attn("self", w, d))
     monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
@@ -199,9 +201,12 @@ def test_split_and_whole_sequence_modes_agree_bitwise(n, monkeypatch):
     _check("self", w, d, torch.from_numpy(split), src, rows, np.array([n]))
 
 
-def test_per_layer_calls_equal_the_stacked_call_bitwise():
+def test_per_layer_calls_equal_the_stacked_call_bitwise(monkeypatch):
     # the model-shaped schedule: one call per layer on offset pointers (a launch of
-    # 16 sequences, which spreads chunks over workgroups) against one stacked launch
+    # 16 sequences, which spreads chunks over workgroups) against one stacked launch.
+    # At the stacked launch's 1024-key chunks the bits agree; left to choose, the
+    # per-layer launch cuts smaller chunks (16 x 3 chunks of 1024 keys would leave most
+    # CUs idle) and stays within the bar of the oracle.
     import autoregressive_audio_token_amd as dec
     w = configs.LONG_OUTPUT
     lens = np.array([2500], np.int32)
@@ -210,11 +215,44 @@ def test_per_layer_calls_equal_the_stacked_call_bitwise():
     nb = dec.dec_attn_workspace_bytes(1, 1, w.heads, 64, w.self_cap, 0)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=hp.DEV)
     dec.dec_attn_workspace_init(ws, nb)
+
+    def per_layer():
+        out = hp.out_buf(w)
+        for layer in range(w.n_layers):
+            dec.dec_attn_self(d["q_self"][layer], d["k_self"][layer], d["v_self"][layer],
+                              d["len"], out[layer], 1, 1, w.heads, w.self_cap, 64, dec.DEC_BF16,
+                              w.scale, ws, nb)
+        return hp.host(out)
+    chosen = per_layer()
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "1024")
+    assert np.array_equal(per_layer(), stacked)
+    src = RowSource(w, lens, d["cross_len_host"])
+    rows = sampled_rows(w, 48, seed=2500)
+    _check("self", w, d, torch.from_numpy(chosen), src, rows, lens)
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+@pytest.mark.parametrize("n", [1, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1000, 2049,
+                               4096])
+def test_small_chunks_ragged_lengths(n, chunk, monkeypatch):
+    # a launch of few sequences (16 heads of one layer) cut into 128- or 256-key chunks,
+    # each its own work item, folded by the last to arrive: every chunk edge
+    import autoregressive_audio_token_amd as dec
+    w = configs.MINI_V1
+    lens = np.array([n], np.int32)
+    d = _inputs(w, self_lens=lens)
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", str(chunk))
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
+    nb = dec.dec_attn_workspace_bytes(1, 1, w.heads, 64, w.self_cap, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=hp.DEV)
+    dec.dec_attn_workspace_init(ws, nb)
     out = hp.out_buf(w)
-    for layer in range(w.n_layers):
+    for layer in (0, w.n_layers - 1):
         dec.dec_attn_self(d["q_self"][layer], d["k_self"][layer], d["v_self"][layer], d["len"],
                           out[layer], 1, 1, w.heads, w.self_cap, 64, dec.DEC_BF16, w.scale, ws, nb)
-    assert np.array_equal(hp.host(out), stacked)
+    src = RowSource(w, lens, d["cross_len_host"])
+    rows = [(layer, 0, h) for layer in (0, w.n_layers - 1) for h in range(w.heads)]
+    _check("self", w, d, out, src, rows, lens)
 
 
 def test_split_combine_is_stable_over_many_back_to_back_runs():
