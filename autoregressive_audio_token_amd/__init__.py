@@ -13,6 +13,11 @@ import importlib
 def __getattr__(name):
     if name.startswith("__"):
         raise AttributeError(name)
+    if name == "build":
+        # `from autoregressive_audio_token_amd import build` asks for this attribute first;
+        # answering through the binding would load the old library before the compile,
+        # and the process would keep that copy (a second load of the path returns it)
+        return importlib.import_module(__name__ + ".build")
     mod = importlib.import_module(__name__ + ".decstep")
     if name == "decstep":
         return mod

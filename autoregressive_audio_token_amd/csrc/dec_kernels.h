@@ -106,6 +106,10 @@ struct SampleParams {
   int B, n_cb, V_valid, V_stride, top_k, fill;
   int rng;                  // 1: uniforms from Philox4x64-10 at counter (step, b, c, 0)
   int logits_bf16;
+  // advance in the same launch: step is then [B, n_cb] (one counter per row) and row r
+  // writes step[r] + 1 back; row (b, 0) adds one to len[b] when len_inc is not null
+  int32_t* step_inc;
+  int32_t* len_inc;
 };
 
 hipError_t sample_launch(const SampleParams& p, hipStream_t stream);

@@ -359,10 +359,11 @@ int dec_sample_topk_philox(const float* logits, int B, int n_cb, int V_valid, in
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
-int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
-                       int V_stride, const float* temperature, int top_k, const float* uniforms,
-                       uint64_t seed, const int32_t* step, int32_t fill_token, int32_t* tokens,
-                       int32_t* topk_idx, float* topk_prob, dec_stream_t stream) {
+// The widened sampler's checks and launch, with the optional in-launch advance.
+static int sample_ex(const void* logits, int logits_dtype, int B, int n_cb, int V_valid, int V_stride,
+              const float* temperature, int top_k, const float* uniforms, uint64_t seed,
+              const int32_t* step, int32_t* step_inc, int32_t* len_inc, int32_t fill_token,
+              int32_t* tokens, int32_t* topk_idx, float* topk_prob, dec_stream_t stream) {
   if (!logits || !temperature || !tokens) return DEC_E_NULL;
   if (logits_dtype != DEC_BF16 && logits_dtype != DEC_F32) return DEC_E_DTYPE;
   if (B < 1 || n_cb < 1 || V_valid < 1 || V_stride < V_valid) return DEC_E_SHAPE;
@@ -372,12 +373,14 @@ int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, in
   if ((long long)B * n_cb * top_k > (1LL << 46)) return DEC_E_SHAPE;
   if (V_valid > dec::kSampMaxVocab) return DEC_E_UNSUPPORTED;
   if (!aligned(logits, logits_dtype == DEC_F32 ? 4 : 2) || !aligned(temperature, 4) ||
-      !aligned(uniforms, 4) || !aligned(step, 4) || !aligned(tokens, 4) ||
+      !aligned(uniforms, 4) || !aligned(step, 4) || !aligned(len_inc, 4) || !aligned(tokens, 4) ||
       !aligned(topk_idx, 4) || !aligned(topk_prob, 4))
     return DEC_E_ALIGN;
   dec::SampleParams p{};
   p.logits = logits;
   p.logits_bf16 = logits_dtype == DEC_BF16;
+  p.step_inc = step_inc;
+  p.len_inc = len_inc;
   p.temperature = temperature;
   p.uniforms = uniforms;
   p.rng = uniforms == nullptr;
@@ -394,6 +397,26 @@ int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, in
   p.fill = fill_token;
   const hipError_t e = dec::sample_launch(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
+                       int V_stride, const float* temperature, int top_k, const float* uniforms,
+                       uint64_t seed, const int32_t* step, int32_t fill_token, int32_t* tokens,
+                       int32_t* topk_idx, float* topk_prob, dec_stream_t stream) {
+  return sample_ex(logits, logits_dtype, B, n_cb, V_valid, V_stride, temperature, top_k,
+                   uniforms, seed, step, nullptr, nullptr, fill_token, tokens, topk_idx,
+                   topk_prob, stream);
+}
+
+int dec_sample_topk_advance(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
+                            int V_stride, const float* temperature, int top_k,
+                            const float* uniforms, uint64_t seed, int32_t* step, int32_t* len,
+                            int32_t fill_token, int32_t* tokens, int32_t* topk_idx,
+                            float* topk_prob, dec_stream_t stream) {
+  if (step == nullptr) return DEC_E_NULL;
+  return sample_ex(logits, logits_dtype, B, n_cb, V_valid, V_stride, temperature, top_k,
+                   uniforms, seed, step, step, len, fill_token, tokens, topk_idx, topk_prob,
+                   stream);
 }
 
 int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

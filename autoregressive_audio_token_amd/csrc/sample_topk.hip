@@ -315,7 +315,11 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   const int b = row / p.n_cb;
   const int c = row - b * p.n_cb;
   const float T = p.temperature[b];
-  const int st = p.step != nullptr ? p.step[b] : 0;
+  const int st = p.step != nullptr ? p.step[p.step_inc != nullptr ? row : b] : 0;
+  if (p.step_inc != nullptr && lane == 0) {  // every counter is read by its own row only
+    p.step_inc[row] = st + 1;
+    if (c == 0 && p.len_inc != nullptr) p.len_inc[b] += 1;  // nothing here reads len
+  }
   const int started = p.step != nullptr ? (st >= c) : 1;
   float u;
   if (p.rng) {  // counter (step, b, c, 0), key (seed, 0): top 24 bits of word 0

@@ -65,6 +65,8 @@ _SIGS = {
                                     ctypes.c_int32, _P, _P, _P, _P]),
     "dec_sample_topk_ex": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, ctypes.c_uint64, _P,
                                 ctypes.c_int32, _P, _P, _P, _P]),
+    "dec_sample_topk_advance": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, ctypes.c_uint64,
+                                     _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "dec_kv_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "dec_lm_head": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "dec_embed_sum": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
@@ -206,6 +208,15 @@ def dec_sample_topk_philox(logits, B, n_cb, V_valid, V_stride, temperature, top_
                                        _ptr(temperature), top_k, seed, _ptr(step), fill_token,
                                        _ptr(tokens), _ptr(topk_idx), _ptr(topk_prob),
                                        _stream(stream)))
+
+
+def dec_sample_topk_advance(logits, logits_dtype, B, n_cb, V_valid, V_stride, temperature,
+                            top_k, uniforms, seed, step, len, fill_token, tokens, topk_idx=None,
+                            topk_prob=None, stream=None):
+    _check(_lib.dec_sample_topk_advance(_ptr(logits), logits_dtype, B, n_cb, V_valid, V_stride,
+                                        _ptr(temperature), top_k, _ptr(uniforms), seed,
+                                        _ptr(step), _ptr(len), fill_token, _ptr(tokens),
+                                        _ptr(topk_idx), _ptr(topk_prob), _stream(stream)))
 
 
 def dec_sample_topk_ex(logits, logits_dtype, B, n_cb, V_valid, V_stride, temperature, top_k,

@@ -112,8 +112,9 @@ def read_probe(dec, torch, nbytes, dev, stream, launches, min_pool=1 << 30):
 def decode_loop(a):
     """The whole generation of a workload with a step count: step s attends over s + 1 self
     keys (and the description), samples with Philox uniforms drawn from (seed, step) and
-    the delay mask, then advances the lengths and steps on the device.  Graphs of R steps
-    (one per cache set) are replayed n_steps / R times and timed end to end."""
+    the delay mask, and advances the lengths and steps on the device in the sampler's own
+    launch (two graph nodes per step).  Graphs of R steps (one per cache set) are replayed
+    n_steps / R times and timed end to end."""
     import numpy as np
     import torch
     import autoregressive_audio_token_amd as dec
@@ -150,7 +151,8 @@ def decode_loop(a):
     o_s = torch.empty((w.n_layers, B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
     o_c = torch.empty_like(o_s)
     tok = torch.empty((B, w.n_codebooks), dtype=torch.int32, device=dev)
-    len_d, step_d = d["len"], d["step"]
+    len_d = d["len"]
+    step_d = torch.zeros((B, w.n_codebooks), dtype=torch.int32, device=dev)  # one per row
     seed = 0x5EED_0000_0000_0004
     stream = torch.cuda.Stream(device=dev)
 
@@ -158,10 +160,9 @@ def decode_loop(a):
         dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], len_d, w.self_cap, o_s,
                           d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
                           o_c, w.n_layers, B, w.heads, w.head_dim, code, w.scale, ws, nb, s)
-        dec.dec_sample_topk_philox(d["logits"], B, w.n_codebooks, w.vocab_valid, w.vocab_stride,
-                                   d["temperature"], w.top_k, seed, step_d, w.fill_token, tok,
-                                   None, None, s)
-        dec.dec_step_advance(len_d, step_d, B, s)
+        dec.dec_sample_topk_advance(d["logits"], dec.DEC_F32, B, w.n_codebooks, w.vocab_valid,
+                                    w.vocab_stride, d["temperature"], w.top_k, None, seed,
+                                    step_d, len_d, w.fill_token, tok, None, None, s)
 
     def reset():
         len_d.fill_(1)
@@ -208,12 +209,12 @@ def decode_loop(a):
                    "cross_cap": w.cross_cap, "top_k": w.top_k, "cache_sets": R,
                    "valid_kv_bytes_total": int(total_bytes),
                    "schedule": f"decode loop: graphs of {R} steps (dec_attn_step + "
-                               f"dec_sample_topk_philox + dec_step_advance, one cache set per "
-                               f"step) replayed {S // R} times; lengths and steps advance on "
-                               f"the device"},
+                               f"dec_sample_topk_advance, one cache set per step) replayed "
+                               f"{S // R} times; lengths and steps advance on the device, in "
+                               f"the sampler's launch"},
         "total_ms": round(total_ms, 3),
         "total_ms_at_70pct_of_peak": round(total_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 3),
-        "roofline": {"bound": "hbm", "kernel": "whole step (attention + sampler + advance)",
+        "roofline": {"bound": "hbm", "kernel": "whole step (attention + sampler with advance)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "checks": {"outputs_finite": out_ok, "tokens_in_range": tok_ok,

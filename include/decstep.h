@@ -250,6 +250,25 @@ int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, in
                        uint64_t seed, const int32_t* step, int32_t fill_token, int32_t* tokens,
                        int32_t* topk_idx, float* topk_prob, dec_stream_t stream);
 
+/* The widened sampler with the step's state advance in the same launch, so a
+ * captured decode step needs no separate advance node ("Analysis and
+ * improvements": the step is one graph with nothing left for the host).
+ * Sampling, arguments, outputs and errors as dec_sample_topk_ex, except:
+ *   step  [B, n_cb] int32, required (DEC_E_NULL): one counter per row, every
+ *         row of sequence b holding the sequence's step (the delay mask and the
+ *         Philox counter read row (b, c)'s own counter); the launch adds one to
+ *         each, so no row reads a counter another row writes
+ *   len   [B] int32 or NULL: the launch adds one to len[b] (the self-attention
+ *         length of the next step); 4-byte aligned
+ * After the launch every step counter and every len[b] is one larger; tokens,
+ * top-k sets and probabilities equal those of dec_sample_topk_ex with step[b]
+ * = the counters' value.  Calls on one state must be stream-ordered. */
+int dec_sample_topk_advance(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
+                            int V_stride, const float* temperature, int top_k,
+                            const float* uniforms, uint64_t seed, int32_t* step, int32_t* len,
+                            int32_t fill_token, int32_t* tokens, int32_t* topk_idx,
+                            float* topk_prob, dec_stream_t stream);
+
 /* Write the current token's key and value rows into the static caches
  * ("Analysis and improvements": caches preallocated at a fixed capacity, so a
  * step writes the next row instead of growing a tensor).

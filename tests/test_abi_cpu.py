@@ -56,6 +56,16 @@ def test_build_module_imports_without_the_library():
     assert r.returncode == 0 and r.stdout.strip().endswith("libdecstep.so")
 
 
+def test_importing_build_from_the_package_loads_no_library():
+    # the build step must not bind the library it is about to replace: a process keeps
+    # the first copy it loads, so the fresh build's new entry points would be missing
+    code = ("import sys; from autoregressive_audio_token_amd import build; "
+            "print('autoregressive_audio_token_amd.decstep' in sys.modules, build.__name__)")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["False", "autoregressive_audio_token_amd.build"]
+
+
 def test_strerror_names_every_status():
     for code in range(8):
         assert dec.dec_strerror(code).startswith("DEC_")
@@ -287,6 +297,21 @@ def test_widened_sampler_host_validation():
     assert _samp_ex(lg=A + 1, dt=0) == D.DEC_E_ALIGN      # bf16 logits: 2-byte aligned
     assert _samp_ex(u=A + 2) == D.DEC_E_ALIGN
     assert _samp_ex(prob=A + 1) == D.DEC_E_ALIGN
+
+
+@_no_gpu
+def test_advancing_sampler_host_validation():
+    def adv(step=A, len_=A, **kw):
+        a = dict(lg=A, dt=1, B=1, ncb=9, V=1089, S=1096, T=A, k=50, u=None, tok=A)
+        a.update(kw)
+        return D.raw_status("dec_sample_topk_advance", a["lg"], a["dt"], a["B"], a["ncb"],
+                            a["V"], a["S"], a["T"], a["k"], a["u"], 7, step, len_, 1089,
+                            a["tok"], None, None, None)
+    assert adv(step=None) == D.DEC_E_NULL            # the counters it advances are required
+    assert adv(lg=None) == D.DEC_E_NULL
+    assert adv(k=0) == D.DEC_E_SHAPE
+    assert adv(step=A + 2) == D.DEC_E_ALIGN
+    assert adv(len_=A + 2) == D.DEC_E_ALIGN
 
 
 def _append(**kw):

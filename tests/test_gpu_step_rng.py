@@ -5,7 +5,10 @@
   parity, and bit-identical outputs to dec_sample_topk given the oracle's uniforms
   (so the device generator reproduces the oracle's Philox words exactly);
 * a captured step -- append, fused attention, sampling with device uniforms, advance --
-  replayed several times with no host input, each replay checked against the oracle.
+  replayed several times with no host input, each replay checked against the oracle, with
+  the advance as its own node or inside the sampler (dec_sample_topk_advance);
+* dec_sample_topk_advance equals dec_sample_topk_ex at the counters' step bit for bit, on
+  the narrow and the wide path, and leaves every counter and length one larger.
 """
 import dataclasses
 
@@ -92,15 +95,17 @@ def test_philox_sampler_without_step_uses_step_zero_and_no_delay():
     assert np.all(hp.host(tok) != w.fill_token)
 
 
-def test_self_driving_captured_step_matches_oracle():
+@pytest.mark.parametrize("fused", [False, True])
+def test_self_driving_captured_step_matches_oracle(fused):
     w = dataclasses.replace(configs.MINI_V1, n_layers=4, self_cap=512, self_len=200)
     L0, N, seed = w.self_len, 4, 77
-    print(f"[selfdrive] NL={w.n_layers} L0={L0} replays={N}", flush=True)
+    print(f"[selfdrive] NL={w.n_layers} L0={L0} replays={N} fused_advance={fused}", flush=True)
     d = wdev.step_inputs(w, hp.DEV)
     kn, vn = gen.new_rows(w, "k", 0), gen.new_rows(w, "v", 0)
     kn_d, vn_d = _dev(kn), _dev(vn)
     len_g = torch.tensor([L0], dtype=torch.int32, device=hp.DEV)
     step_g = torch.tensor([0], dtype=torch.int32, device=hp.DEV)
+    step_rows = torch.zeros((1, 9), dtype=torch.int32, device=hp.DEV)   # fused: one per row
     ws, nb = hp.workspace(w, w.self_cap, w.cross_cap)
     o_s, o_c = hp.out_buf(w), hp.out_buf(w)
     tok = torch.zeros((1, 9), dtype=torch.int32, device=hp.DEV)
@@ -115,10 +120,15 @@ def test_self_driving_captured_step_matches_oracle():
         dec.dec_attn_step(d["q_self"], d["k_self"], d["v_self"], len_g, w.self_cap, o_s,
                           d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"], w.cross_cap,
                           o_c, w.n_layers, 1, w.heads, 64, dec.DEC_BF16, w.scale, ws, nb, s)
-        dec.dec_sample_topk_philox(d["logits"], 1, 9, w.vocab_valid, w.vocab_stride,
-                                   d["temperature"], w.top_k, seed, step_g, w.fill_token, tok,
-                                   idx, prob, s)
-        dec.dec_step_advance(len_g, step_g, 1, s)
+        if fused:
+            dec.dec_sample_topk_advance(d["logits"], dec.DEC_F32, 1, 9, w.vocab_valid,
+                                        w.vocab_stride, d["temperature"], w.top_k, None, seed,
+                                        step_rows, len_g, w.fill_token, tok, idx, prob, s)
+        else:
+            dec.dec_sample_topk_philox(d["logits"], 1, 9, w.vocab_valid, w.vocab_stride,
+                                       d["temperature"], w.top_k, seed, step_g, w.fill_token,
+                                       tok, idx, prob, s)
+            dec.dec_step_advance(len_g, step_g, 1, s)
         exe = dec.dec_graph_end(s)
 
     # oracle state: generator rows below L0 - 1, then the appended row at every later slot
@@ -142,10 +152,56 @@ def test_self_driving_captured_step_matches_oracle():
             u = orng.sample_uniforms(seed, [i], 9)
             _compare(lg, w.vocab_valid, T, w.top_k, u, np.array([i], np.int32), w.fill_token,
                      tok, idx, prob)
-            assert hp.host(len_g)[0] == n + 1 and hp.host(step_g)[0] == i + 1
+            assert hp.host(len_g)[0] == n + 1
+            if fused:
+                assert np.all(hp.host(step_rows) == i + 1)
+            else:
+                assert hp.host(step_g)[0] == i + 1
         kc = _bits(d["k_self"])[:, 0]
         for l in range(w.n_layers):
             for j in range(L0 - 1, L0 - 1 + N):
                 assert np.array_equal(kc[l, :, j], kn[l, 0]), (l, j)
+    finally:
+        dec.dec_graph_destroy(exe)
+
+
+@pytest.mark.parametrize("k,uniforms", [(50, False), (50, True), (250, False)])
+def test_advancing_sampler_equals_sampler_at_each_step(k, uniforms):
+    # 12 captured replays from steps 0, 3, 8, 9, 100 (the delay mask opens codebook by
+    # codebook for the first rows); each replay equals dec_sample_topk_ex at that step
+    B, n_cb, V, S, seed = 5, 9, 1089, 1096, 0x0123_4567_89AB_CDEF
+    rng = np.random.default_rng(7 + k)
+    lg = np.full((B, n_cb, S), 1e30, np.float32)
+    lg[:, :, :V] = rng.standard_normal((B, n_cb, V), dtype=np.float32) * 3
+    T = np.array([1.0, 0.0, 0.7, 1.3, 1.0], np.float32)
+    step0 = np.array([0, 3, 8, 9, 100], np.int32)
+    len0 = np.array([10, 20, 30, 40, 50], np.int32)
+    print(f"[advance] k={k} uniforms={uniforms}", flush=True)
+    lg_d, T_d = _dev(lg), _dev(T)
+    u_d = _dev(rng.random((B, n_cb), dtype=np.float32)) if uniforms else None
+    step_rows = _dev(np.repeat(step0[:, None], n_cb, 1))
+    len_d = _dev(len0)
+    outs = [torch.zeros((B, n_cb), dtype=torch.int32, device=hp.DEV),
+            torch.zeros((B, n_cb, k), dtype=torch.int32, device=hp.DEV),
+            torch.zeros((B, n_cb, k), dtype=torch.float32, device=hp.DEV)]
+    refs = [torch.empty_like(t) for t in outs]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dec.dec_graph_begin(s)
+        dec.dec_sample_topk_advance(lg_d, dec.DEC_F32, B, n_cb, V, S, T_d, k, u_d, seed,
+                                    step_rows, len_d, 1089, *outs, s)
+        exe = dec.dec_graph_end(s)
+    try:
+        for i in range(12):
+            dec.dec_graph_launch(exe, s)
+            s.synchronize()
+            dec.dec_sample_topk_ex(lg_d, dec.DEC_F32, B, n_cb, V, S, T_d, k, u_d, seed,
+                                   _dev(step0 + i), 1089, *refs)
+            torch.cuda.synchronize()
+            for a, r in zip(outs, refs):
+                assert np.array_equal(_bits(a), _bits(r)), f"replay {i}"
+            assert np.array_equal(hp.host(step_rows), np.repeat(step0[:, None] + i + 1, n_cb, 1))
+            assert np.array_equal(hp.host(len_d), len0 + i + 1)
     finally:
         dec.dec_graph_destroy(exe)
