@@ -457,8 +457,8 @@ def cpu_baseline(w, seconds):
 def main(argv=None):
     a = parse(argv)
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has "
-              "no multi-GPU path: every GPU box here has a single MI355X.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}): the library has "
+              "no multi-GPU path; the work is sized for a single MI355X.", file=sys.stderr)
         return 2
     if a.copy_mib > 0:
         return copy_calibration(a.copy_mib)
