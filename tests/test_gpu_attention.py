@@ -268,3 +268,34 @@ def test_split_combine_is_stable_over_many_back_to_back_runs():
         assert np.array_equal(hp.host(o_s), ref_s) and np.array_equal(hp.host(o_c), ref_c)
     src = RowSource(w, d["self_len_host"], d["cross_len_host"])
     _check("cross", w, d, outs[-1][1], src, all_rows(w), d["cross_len_host"])
+
+
+def test_self_cross_and_step_calls_share_one_workspace():
+    # One workspace serves dec_attn_self, dec_attn_cross and dec_attn_step of one shape.
+    # These launches (few sequences) spread chunks over workgroups and may each choose a
+    # different chunk, so their chunk states sit at different places; the arrival tickets
+    # must stay where every call expects them and return to zero.  Interleaved calls, in
+    # stream order, each within the bar of the oracle and repeating bit for bit.  The
+    # description cache holds more chunks than the self cache: a layout that put the step's
+    # cross tickets after the self chunk states let a cross-only call's states cover them.
+    import dataclasses
+    w = dataclasses.replace(configs.MINI_V1, n_layers=2, self_cap=2048, self_len=1500,
+                            cross_cap=4096, cross_len=3000)
+    d = _inputs(w)
+    s_len, c_len = d["self_len_host"], d["cross_len_host"]
+    ws = hp.workspace(w, w.self_cap, w.cross_cap)
+    runs = []
+    for _ in range(3):
+        o_self = hp.host(hp.attn("self", w, d, ws=ws))
+        o_step = [hp.host(t) for t in hp.attn_step(w, d, ws)]
+        o_cross = hp.host(hp.attn("cross", w, d, ws=ws))
+        runs.append((o_self, *o_step, o_cross))
+    for later in runs[1:]:
+        for a, b in zip(runs[0], later):
+            assert np.array_equal(a, b)
+    src = RowSource(w, s_len, c_len)
+    rows = all_rows(w)
+    o_self, s_step, c_step, o_cross = runs[0]
+    for kind, out, lens in (("self", o_self, s_len), ("self", s_step, s_len),
+                            ("cross", c_step, c_len), ("cross", o_cross, c_len)):
+        _check(kind, w, d, torch.from_numpy(out), src, rows, lens)
