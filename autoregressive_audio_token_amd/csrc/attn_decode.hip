@@ -228,6 +228,28 @@ struct Tile {
     }
   }
 
+  // The key `row` of the sequence, if this tile holds it, becomes the lanes' slices kn, vn
+  // (the current token's rows, which the cache does not hold yet); the lanes holding it
+  // also write them to that row of the sequence's cache (kseq, vseq; this lane's slice at
+  // element offset `slice`).  Uniform test: one tile per sequence takes the branch.
+  __device__ __forceinline__ void put_row(int base, int row, int kg, const u32x4& kn,
+                                          const u32x4& vn, const T* kseq, const T* vseq,
+                                          int slice) {
+    const int j = row - base;
+    if ((unsigned)j >= (unsigned)KPT) return;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const bool mine = j == i * KPL + kg;
+      k[i] = mine ? kn : k[i];
+      v[i] = mine ? vn : v[i];
+    }
+    if (j % KPL == kg) {
+      const size_t off = (size_t)row * HD + slice;
+      *reinterpret_cast<u32x4*>(const_cast<T*>(kseq) + off) = kn;
+      *reinterpret_cast<u32x4*>(const_cast<T*>(vseq) + off) = vn;
+    }
+  }
+
   // Online-softmax update of this lane group's state (m, l, acc) with the tile.
   // MASK: bit j of `keep` says whether key base + j is attended (a boolean key mask).
   template <bool MASK = false>
@@ -289,7 +311,7 @@ __device__ __forceinline__ void store_out(const AttnSeg& S, size_t i, float a, f
 // the pool (a tile of at most 64 keys never crosses a block); other segments read the
 // static layout.  EX: the widened entry point -- segments with a key bitmask skip the
 // keys whose bit is clear, and outputs may be bf16.  HD: head dim, 64 or 128.
-template <typename T, bool PAGED, bool EX, int HD>
+template <typename T, bool PAGED, bool EX, int HD, bool APP = false>
 __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p) {
   using TileT = Tile<T, HD>;
   constexpr int EPL = TileT::EPL;
@@ -481,6 +503,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const int none = paged ? 0 : n;
     float fm = 0.f, fl = 0.f, fa = 0.f;  // running fold (combining threads)
     const T* qp = static_cast<const T*>(S.q) + wave_sidx * HD + dl * EPL;
+    // the current token's rows (static caches): key n - 1 is taken from k_new / v_new and
+    // written to the cache by the lanes that hold it; a length past the capacity appends
+    // nothing (the cache's rows are read as they are)
+    int app_row = -1;
+    u32x4 kn = {0u, 0u, 0u, 0u}, vn = {0u, 0u, 0u, 0u};
+    if (APP && S.k_new != nullptr) {  // uniform: the self segment of an appending launch
+      if (S.len[b] <= S.L_cap) app_row = n - 1;
+      const size_t src = wave_sidx * HD + dl * EPL;
+      kn = *reinterpret_cast<const u32x4*>(static_cast<const T*>(S.k_new) + src);
+      vn = *reinterpret_cast<const u32x4*>(static_cast<const T*>(S.v_new) + src);
+    }
 
     for (int c = c0; c < c1; ++c) {
       // tile t of this wave starts at key cb + t * kStep; packed items read one tile
@@ -544,10 +577,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           const int base = cb + t * kStep;
           const TileAddr a1 = addr(t + 1);
           tb.load(a1.k, a1.v, a1.row0, lane_off);
+          if constexpr (APP) ta.put_row(base, app_row, kg, kn, vn, kp, vp, dl * EPL);
           ta.template consume<EX>(qs, base, n, kg, m_g, l_g, acc, keep_a);
           if (t + 1 >= nt) break;
           const TileAddr a2 = addr(t + 2);
           ta.load(a2.k, a2.v, a2.row0, lane_off);
+          if constexpr (APP) tb.put_row(base + kStep, app_row, kg, kn, vn, kp, vp, dl * EPL);
           tb.template consume<EX>(qs, base + kStep, n, kg, m_g, l_g, acc, a1.keep);
           keep_a = a2.keep;
         }
@@ -648,21 +683,26 @@ namespace {
 // fields are relaxed atomics: every writer stores the same value.
 struct DevInfo {
   std::atomic<int> cus{0};
-  std::atomic<int> occ[2][2][3] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
+  std::atomic<int> occ[2][2][4] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
 };
 DevInfo g_dev[64];
 
-// variant: 0 static, 1 paged, 2 widened (key masks / bf16 outputs, static caches)
+// variant: 0 static, 1 paged, 2 widened (key masks / bf16 outputs, static caches), 3 static
+// with the current token's rows appended
 template <typename T, int HD>
 void* attn_kernel_ptr(int variant) {
-  return variant == 2   ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, true, HD>)
+  return variant == 3   ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD, true>)
+         : variant == 2 ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, true, HD>)
          : variant == 1 ? reinterpret_cast<void*>(&attn_decode_kernel<T, true, false, HD>)
                         : reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD>);
 }
 
 template <typename T, int HD>
 void attn_kernel_go(int variant, int blocks, size_t lds, hipStream_t stream, const AttnParams& p) {
-  if (variant == 2)
+  if (variant == 3)
+    hipLaunchKernelGGL((attn_decode_kernel<T, false, false, HD, true>), dim3(blocks),
+                       dim3(kAttnThreads), lds, stream, p);
+  else if (variant == 2)
     hipLaunchKernelGGL((attn_decode_kernel<T, false, true, HD>), dim3(blocks), dim3(kAttnThreads),
                        lds, stream, p);
   else if (variant == 1)
@@ -688,7 +728,8 @@ hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_
   const bool paged = p.seg[0].table != nullptr || (p.nseg > 1 && p.seg[1].table != nullptr);
   const bool ex = p.seg[0].mask != nullptr || p.seg[0].out_bf16 ||
                   (p.nseg > 1 && (p.seg[1].mask != nullptr || p.seg[1].out_bf16));
-  const int variant = ex ? 2 : paged ? 1 : 0;
+  const bool app = p.seg[0].k_new != nullptr;  // static, plain: the ABI allows no other
+  const int variant = ex ? 2 : paged ? 1 : app ? 3 : 0;
   const int wide = p.hd == kAttnHeadDimWide ? 1 : 0;
   if (!wide && p.hd != kAttnHeadDim) return hipErrorInvalidValue;
   void* fn = dtype == 0 ? (wide ? attn_kernel_ptr<uint16_t, kAttnHeadDimWide>(variant)

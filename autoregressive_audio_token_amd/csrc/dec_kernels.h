@@ -70,6 +70,11 @@ struct AttnSeg {
   const uint32_t* mask;   // [B, mask_words], mask_words even
   int mask_words;
   int out_bf16;
+  // the current token's rows (static caches): when k_new != nullptr, a sequence with
+  // 1 <= len <= L_cap attends with k_new / v_new as its key len - 1 and the launch writes
+  // them to that slot of k / v
+  const void* k_new;      // [NL, B, H, hd]
+  const void* v_new;
 };
 
 struct AttnParams {

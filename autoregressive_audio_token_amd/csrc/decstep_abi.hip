@@ -86,6 +86,9 @@ struct SegArgs {
   const uint32_t* mask = nullptr;
   int mask_words = 0;
   int out_bf16 = 0;
+  // the current token's rows, appended at slot len[b] - 1 of k / v in the launch
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
 };
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -176,6 +179,8 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
     g.mask = segs[s].mask;
     g.mask_words = segs[s].mask_words;
     g.out_bf16 = segs[s].out_bf16;
+    g.k_new = segs[s].k_new;
+    g.v_new = segs[s].v_new;
     if (lay.bytes > 0) {  // nck_cap follows the chunk the launcher settles on
       char* base = static_cast<char*>(ws);
       g.ticket = reinterpret_cast<int32_t*>(base + s * lay.ticket_bytes);
@@ -237,6 +242,22 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self, co
                   size_t ws_bytes, dec_stream_t stream) {
   const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
                         {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_step_append(const void* q_self, void* k_self, void* v_self, const int32_t* len,
+                         int L_cap_self, float* out_self, const void* k_new, const void* v_new,
+                         const void* q_cross, const void* k_cross, const void* v_cross,
+                         const int32_t* enc_len, int L_cap_cross, float* out_cross, int n_layers,
+                         int B, int H, int hd, int dtype, float scale, void* workspace,
+                         size_t ws_bytes, dec_stream_t stream) {
+  if (k_new == nullptr || v_new == nullptr) return DEC_E_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return DEC_E_ALIGN;
+  SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
+                  {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  s[0].k_new = k_new;
+  s[0].v_new = v_new;
   return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
                      reinterpret_cast<hipStream_t>(stream));
 }

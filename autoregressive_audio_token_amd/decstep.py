@@ -53,6 +53,8 @@ _SIGS = {
     "dec_attn_cross": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_attn_step": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _P,
                            _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "dec_attn_step_append": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                  _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_attn_step_ex": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P,
                               _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_attn_self_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -153,6 +155,16 @@ def dec_attn_cross(q, k, v, enc_len, out, n_layers, B, H, L_cap, hd, dtype, scal
     _check(_lib.dec_attn_cross(_ptr(q), _ptr(k), _ptr(v), _ptr(enc_len), _ptr(out), n_layers,
                                B, H, L_cap, hd, dtype, scale, _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+def dec_attn_step_append(q_self, k_self, v_self, len, L_cap_self, out_self, k_new, v_new,
+                         q_cross, k_cross, v_cross, enc_len, L_cap_cross, out_cross,
+                         n_layers, B, H, hd, dtype, scale, workspace, ws_bytes, stream=None):
+    _check(_lib.dec_attn_step_append(_ptr(q_self), _ptr(k_self), _ptr(v_self), _ptr(len),
+                                     L_cap_self, _ptr(out_self), _ptr(k_new), _ptr(v_new),
+                                     _ptr(q_cross), _ptr(k_cross), _ptr(v_cross), _ptr(enc_len),
+                                     L_cap_cross, _ptr(out_cross), n_layers, B, H, hd, dtype,
+                                     scale, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dec_attn_step(q_self, k_self, v_self, len, L_cap_self, out_self,

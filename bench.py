@@ -71,6 +71,9 @@ def parse(argv=None):
     ap.add_argument("--decode-loop", action="store_true",
                     help="a workload with a step count (long_output): the whole generation,\n"
                          "lengths and steps advanced on the device, timed end to end")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="with --decode-loop: append the current token's rows with\n"
+                         "dec_kv_append as a node of its own (for comparison)")
     ap.add_argument("--calibrate", action="store_true",
                     help="the calibration kernels: streaming reads at 4 MiB, the workload's\n"
                          "valid bytes and 4 GiB, and the cost of an empty graph node")
@@ -110,15 +113,16 @@ def read_probe(dec, torch, nbytes, dev, stream, launches, min_pool=1 << 30):
 
 
 def decode_loop(a):
-    """The whole generation of a workload with a step count: step s attends over s + 1 self
-    keys (and the description), samples with Philox uniforms drawn from (seed, step) and
-    the delay mask, and advances the lengths and steps on the device in the sampler's own
-    launch (two graph nodes per step).  Graphs of R steps (one per cache set) are replayed
-    n_steps / R times and timed end to end."""
+    """The whole generation of a workload with a step count: step s appends the current
+    token's key and value rows and attends over s + 1 self keys (and the description) in
+    one launch, then samples with Philox uniforms drawn from (seed, step) and the delay mask
+    and advances the lengths and steps in the sampler's own launch: two graph nodes per
+    step.  Graphs of R steps (one per cache set) are replayed n_steps / R times and timed
+    end to end."""
     import numpy as np
     import torch
     import autoregressive_audio_token_amd as dec
-    from workloads import configs, device as wdev
+    from workloads import configs, gen, device as wdev
 
     w = configs.BY_NAME[a.workload]
     if w.n_steps <= 1:
@@ -151,15 +155,27 @@ def decode_loop(a):
     o_s = torch.empty((w.n_layers, B, w.heads, w.head_dim), dtype=torch.float32, device=dev)
     o_c = torch.empty_like(o_s)
     tok = torch.empty((B, w.n_codebooks), dtype=torch.int32, device=dev)
+    k_new = wdev.to_device(gen.new_rows(w, "k", 0), dev)      # the current token's rows
+    v_new = wdev.to_device(gen.new_rows(w, "v", 0), dev)
     len_d = d["len"]
     step_d = torch.zeros((B, w.n_codebooks), dtype=torch.int32, device=dev)  # one per row
     seed = 0x5EED_0000_0000_0004
     stream = torch.cuda.Stream(device=dev)
 
     def step(st, s):
-        dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], len_d, w.self_cap, o_s,
-                          d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
-                          o_c, w.n_layers, B, w.heads, w.head_dim, code, w.scale, ws, nb, s)
+        if a.separate_append:
+            dec.dec_kv_append(k_new, v_new, st["k_self"], st["v_self"], len_d, w.n_layers, B,
+                              w.heads, w.self_cap, w.head_dim, code, s)
+            dec.dec_attn_step(d["q_self"], st["k_self"], st["v_self"], len_d, w.self_cap, o_s,
+                              d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"],
+                              w.cross_cap, o_c, w.n_layers, B, w.heads, w.head_dim, code,
+                              w.scale, ws, nb, s)
+        else:
+            dec.dec_attn_step_append(d["q_self"], st["k_self"], st["v_self"], len_d,
+                                     w.self_cap, o_s, k_new, v_new, d["q_cross"],
+                                     st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap,
+                                     o_c, w.n_layers, B, w.heads, w.head_dim, code, w.scale,
+                                     ws, nb, s)
         dec.dec_sample_topk_advance(d["logits"], dec.DEC_F32, B, w.n_codebooks, w.vocab_valid,
                                     w.vocab_stride, d["temperature"], w.top_k, None, seed,
                                     step_d, len_d, w.fill_token, tok, None, None, s)
@@ -208,13 +224,18 @@ def decode_loop(a):
                    "self_cap": w.self_cap, "cross_len": [int(x) for x in c_len][:4],
                    "cross_cap": w.cross_cap, "top_k": w.top_k, "cache_sets": R,
                    "valid_kv_bytes_total": int(total_bytes),
-                   "schedule": f"decode loop: graphs of {R} steps (dec_attn_step + "
-                               f"dec_sample_topk_advance, one cache set per step) replayed "
-                               f"{S // R} times; lengths and steps advance on the device, in "
-                               f"the sampler's launch"},
+                   "schedule": (f"decode loop: graphs of {R} steps (dec_kv_append, "
+                                f"dec_attn_step, dec_sample_topk_advance: three nodes; one "
+                                f"cache set per step) replayed {S // R} times"
+                                if a.separate_append else
+                                f"decode loop: graphs of {R} steps (dec_attn_step_append: "
+                                f"the current token's rows appended and attended in one "
+                                f"launch; dec_sample_topk_advance: sampling and the length "
+                                f"and step advance in one launch; one cache set per step) "
+                                f"replayed {S // R} times")},
         "total_ms": round(total_ms, 3),
         "total_ms_at_70pct_of_peak": round(total_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 3),
-        "roofline": {"bound": "hbm", "kernel": "whole step (attention + sampler with advance)",
+        "roofline": {"bound": "hbm", "kernel": "whole step (append + attention, sampler + advance)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "checks": {"outputs_finite": out_ok, "tokens_in_range": tok_ok,

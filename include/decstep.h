@@ -129,6 +129,23 @@ int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
                   int n_layers, int B, int H, int hd, int dtype, float scale,
                   void* workspace, size_t ws_bytes, dec_stream_t stream);
 
+/* dec_attn_step with the current token's key and value rows appended to the
+ * static self cache in the same launch ("Analysis and improvements": the
+ * cache is preallocated and a step writes its next row; the whole step is
+ * one graph).  k_new, v_new [n_layers, B, H, hd] dtype, 16-byte aligned.
+ * For a sequence with 1 <= len[b] <= L_cap_self, self-attention uses k_new /
+ * v_new as key len[b] - 1 and the launch writes them to that slot of k_self /
+ * v_self; with len[b] < 1 or len[b] > L_cap_self nothing is written and the
+ * cache is read as it is.  Outputs and caches equal those of dec_kv_append
+ * followed by dec_attn_step bit for bit; one launch instead of two.  Other
+ * arguments, errors and the workspace as dec_attn_step. */
+int dec_attn_step_append(const void* q_self, void* k_self, void* v_self, const int32_t* len,
+                         int L_cap_self, float* out_self, const void* k_new, const void* v_new,
+                         const void* q_cross, const void* k_cross, const void* v_cross,
+                         const int32_t* enc_len, int L_cap_cross, float* out_cross, int n_layers,
+                         int B, int H, int hd, int dtype, float scale, void* workspace,
+                         size_t ws_bytes, dec_stream_t stream);
+
 /* dec_attn_step with two widenings (both optional):
  *   cross_mask  [B, mask_words] uint32, or NULL: an arbitrary boolean mask over
  *               the description ("A rough architecture of Parler TTS": the

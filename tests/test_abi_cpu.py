@@ -300,6 +300,21 @@ def test_widened_sampler_host_validation():
 
 
 @_no_gpu
+def test_fused_append_host_validation():
+    def call(kn=A, vn=A, **kw):
+        a = dict(q=A, len=A, out=A)
+        a.update(kw)
+        return D.raw_status("dec_attn_step_append", a["q"], A, A, a["len"], 4096, a["out"], kn,
+                            vn, A, A, A, A, 1024, A, 24, 1, 16, 64, 0, ctypes.c_float(0.125),
+                            A, 1 << 30, None)
+    assert call(kn=None) == D.DEC_E_NULL
+    assert call(vn=None) == D.DEC_E_NULL
+    assert call(kn=A + 8) == D.DEC_E_ALIGN
+    assert call(len=None) == D.DEC_E_NULL          # then dec_attn_step's own checks
+    assert call(q=A + 8) == D.DEC_E_ALIGN
+
+
+@_no_gpu
 def test_advancing_sampler_host_validation():
     def adv(step=A, len_=A, **kw):
         a = dict(lg=A, dt=1, B=1, ncb=9, V=1089, S=1096, T=A, k=50, u=None, tok=A)

@@ -39,6 +39,11 @@ def _bits(t):
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
 
 
+def d_cross_lens(w):
+    """Rows drawn into the description cache: its capacity."""
+    return np.full(w.batch, w.cross_cap)
+
+
 def _np_bits(a):
     a = np.asarray(a)
     return a.view(np.uint16) if a.dtype == np.uint16 else a.astype(np.float32).view(np.uint32)
@@ -95,11 +100,12 @@ def test_philox_sampler_without_step_uses_step_zero_and_no_delay():
     assert np.all(hp.host(tok) != w.fill_token)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_self_driving_captured_step_matches_oracle(fused):
+@pytest.mark.parametrize("fused,fused_append", [(False, False), (True, False), (True, True)])
+def test_self_driving_captured_step_matches_oracle(fused, fused_append):
     w = dataclasses.replace(configs.MINI_V1, n_layers=4, self_cap=512, self_len=200)
     L0, N, seed = w.self_len, 4, 77
-    print(f"[selfdrive] NL={w.n_layers} L0={L0} replays={N} fused_advance={fused}", flush=True)
+    print(f"[selfdrive] NL={w.n_layers} L0={L0} replays={N} fused_advance={fused} "
+          f"fused_append={fused_append}", flush=True)
     d = wdev.step_inputs(w, hp.DEV)
     kn, vn = gen.new_rows(w, "k", 0), gen.new_rows(w, "v", 0)
     kn_d, vn_d = _dev(kn), _dev(vn)
@@ -115,11 +121,18 @@ def test_self_driving_captured_step_matches_oracle(fused):
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
         dec.dec_graph_begin(s)
-        dec.dec_kv_append(kn_d, vn_d, d["k_self"], d["v_self"], len_g, w.n_layers, 1, w.heads,
-                          w.self_cap, 64, dec.DEC_BF16, s)
-        dec.dec_attn_step(d["q_self"], d["k_self"], d["v_self"], len_g, w.self_cap, o_s,
-                          d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"], w.cross_cap,
-                          o_c, w.n_layers, 1, w.heads, 64, dec.DEC_BF16, w.scale, ws, nb, s)
+        if fused_append:          # append and attention in one launch
+            dec.dec_attn_step_append(d["q_self"], d["k_self"], d["v_self"], len_g, w.self_cap,
+                                     o_s, kn_d, vn_d, d["q_cross"], d["k_cross"], d["v_cross"],
+                                     d["enc_len"], w.cross_cap, o_c, w.n_layers, 1, w.heads, 64,
+                                     dec.DEC_BF16, w.scale, ws, nb, s)
+        else:
+            dec.dec_kv_append(kn_d, vn_d, d["k_self"], d["v_self"], len_g, w.n_layers, 1,
+                              w.heads, w.self_cap, 64, dec.DEC_BF16, s)
+            dec.dec_attn_step(d["q_self"], d["k_self"], d["v_self"], len_g, w.self_cap, o_s,
+                              d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"],
+                              w.cross_cap, o_c, w.n_layers, 1, w.heads, 64, dec.DEC_BF16,
+                              w.scale, ws, nb, s)
         if fused:
             dec.dec_sample_topk_advance(d["logits"], dec.DEC_F32, 1, 9, w.vocab_valid,
                                         w.vocab_stride, d["temperature"], w.top_k, None, seed,
@@ -205,3 +218,37 @@ def test_advancing_sampler_equals_sampler_at_each_step(k, uniforms):
             assert np.array_equal(hp.host(len_d), len0 + i + 1)
     finally:
         dec.dec_graph_destroy(exe)
+
+
+@pytest.mark.parametrize("split,chunk", [("0", None), ("1", None), ("1", "128"), ("1", "256")])
+def test_fused_append_equals_append_then_attention(split, chunk, monkeypatch):
+    # dec_attn_step_append against dec_kv_append + dec_attn_step on copies of the same
+    # caches: outputs and both caches bit for bit.  Lengths at tile and chunk edges, the
+    # full capacity, past it and non-positive (those append nothing).
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    if chunk:
+        monkeypatch.setenv("DECSTEP_ATTN_CHUNK", chunk)
+    lens = np.array([1, 2, 32, 33, 64, 65, 129, 1024, 1025, 2048, 2049, 3000, 0, -3], np.int32)
+    w = dataclasses.replace(configs.MINI_V1, n_layers=2, batch=len(lens), self_cap=2048,
+                            self_len=None, self_len_range=(1, 2))
+    print(f"[fused append] split={split} chunk={chunk} lens={lens.tolist()}", flush=True)
+    d = wdev.step_inputs(w, hp.DEV, self_lens=lens,
+                         fill_lens=(np.full(len(lens), w.self_cap), d_cross_lens(w)))
+    kn, vn = _dev(gen.new_rows(w, "k", 3)), _dev(gen.new_rows(w, "v", 3))
+    ws, nb = hp.workspace(w, w.self_cap, w.cross_cap)
+    k2, v2 = d["k_self"].clone(), d["v_self"].clone()
+    ref_s, ref_c = hp.out_buf(w), hp.out_buf(w)
+    dec.dec_kv_append(kn, vn, k2, v2, d["len"], w.n_layers, w.batch, w.heads, w.self_cap, 64,
+                      dec.DEC_BF16)
+    dec.dec_attn_step(d["q_self"], k2, v2, d["len"], w.self_cap, ref_s, d["q_cross"],
+                      d["k_cross"], d["v_cross"], d["enc_len"], w.cross_cap, ref_c, w.n_layers,
+                      w.batch, w.heads, 64, dec.DEC_BF16, w.scale, ws, nb)
+    o_s, o_c = hp.out_buf(w), hp.out_buf(w)
+    dec.dec_attn_step_append(d["q_self"], d["k_self"], d["v_self"], d["len"], w.self_cap, o_s,
+                             kn, vn, d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"],
+                             w.cross_cap, o_c, w.n_layers, w.batch, w.heads, 64, dec.DEC_BF16,
+                             w.scale, ws, nb)
+    assert np.array_equal(_bits(o_s), _bits(ref_s))
+    assert np.array_equal(_bits(o_c), _bits(ref_c))
+    assert np.array_equal(_bits(d["k_self"]), _bits(k2))
+    assert np.array_equal(_bits(d["v_self"]), _bits(v2))
