@@ -43,6 +43,13 @@ namespace dec {
 
 constexpr int kSurvSlots = 3;                   // survivor slots per lane after pruning
 constexpr int kSurvCap = kSurvSlots * kWave;     // survivors that fit
+// Wide variant: top_k up to kWidePruneK is pruned to at most kWideSlots per lane (the
+// bound below, for t = ceil(top_k / 64) and t + 1, so each lane keeps its kWideMaxT
+// largest keys).
+constexpr int kWidePruneK = 4 * kWave;
+constexpr int kWideMaxT = 5;
+constexpr int kWideSlots = 8;
+constexpr int kWideSurvCap = kWideSlots * kWave;
 
 __device__ __forceinline__ int lanes_below(unsigned long long mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32),
@@ -219,10 +226,11 @@ __device__ __forceinline__ float logit_at(const uint16_t* x, int i) {
 // entry in vocabulary order goes to output position t.
 template <int VPL>
 __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, const uint32_t (&key)[VPL],
-                                            const int (&idx)[VPL], int kk, uint32_t kmax, float T,
-                                            float u, int started, uint32_t* hist) {
+                                            const int (&idx)[VPL], int kk, uint32_t lo,
+                                            uint32_t kmax, float T, float u, int started,
+                                            uint32_t* hist) {
   const int lane = static_cast<int>(__lane_id());
-  const uint32_t tau = radix_tau(key, idx, kk, 0u, kmax, hist);
+  const uint32_t tau = radix_tau(key, idx, kk, lo, kmax, hist);
   int cnt_gt = 0;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) cnt_gt += __popcll(__ballot(key[j] > tau));
@@ -270,14 +278,16 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
 #pragma unroll
     for (int j = 0; j < VPL; ++j) hit[j] = __ballot(pos[j] >= 0 && u < S[j] * rZ);
   }
+  // slots hold entries in vocabulary order (the whole row, or its compacted survivors):
+  // the first slot with a hit wins, and the token is that entry's index
 #pragma unroll
-  for (int j = VPL - 1; j >= 0; --j)  // the first slot with a hit wins
-    if (hit[j]) token = j * kWave + __ffsll(hit[j]) - 1;
+  for (int j = VPL - 1; j >= 0; --j)
+    if (hit[j]) token = __builtin_amdgcn_readlane(idx[j], __ffsll(hit[j]) - 1);
   if (token < 0) {  // rounding left u >= C_last: the last kept entry
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const unsigned long long mk = __ballot(pos[j] == kk - 1);
-      if (mk) token = j * kWave + __ffsll(mk) - 1;
+      if (mk) token = __builtin_amdgcn_readlane(idx[j], __ffsll(mk) - 1);
     }
   }
   if (lane == 0) p.tokens[row] = started ? token : p.fill;
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   // [0, kSurvCap) plus one dummy slot per lane
   __shared__ float s_val[kSampWaves][2 * kWave];
   __shared__ int s_idx[kSampWaves][2 * kWave];
-  __shared__ uint2 s_surv[kSampWaves][kSurvCap + kWave];
+  __shared__ uint2 s_surv[kSampWaves][(WIDE ? kWideSurvCap : kSurvCap) + kWave];
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSampWaves][kHistWords];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -350,7 +360,71 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
   }
   const uint32_t kmax = wave_max_key(lmax);
   if constexpr (WIDE) {
-    sample_wide(p, row, key, idx, kk, kmax, T, u, started, s_hist[wave]);
+    if constexpr (VPL > kWideSlots) {
+      // Pruning: for any t with c = ceil(kk / t) <= 64, each lane holds t keys at least as
+      // large as its t-th largest a_l, so at least t * c >= kk keys reach the c-th largest
+      // a_l: that bounds the kk-th largest key from below, and so does the larger of the
+      // bounds for t = ceil(kk / 64) and t + 1 (the second is often the tighter: at the
+      // first, c is often 64, the smallest a_l).  Every entry the kept set can hold, ties
+      // included, survives.
+      const int t0 = (kk + kWave - 1) / kWave;
+      if (kk <= kWidePruneK) {
+        uint32_t top[kWideMaxT];  // this lane's largest keys, descending
+#pragma unroll
+        for (int i = 0; i < kWideMaxT; ++i) top[i] = 0u;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          uint32_t x = key[j];
+#pragma unroll
+          for (int i = 0; i < kWideMaxT; ++i) {
+            const uint32_t hi = top[i] > x ? top[i] : x;
+            x = top[i] > x ? x : top[i];
+            top[i] = hi;
+          }
+        }
+        // a_l for t0 and t0 + 1 (t0 is 2, 3 or 4 here); both searches run interleaved, to
+        // 18 leading bits (independent chains)
+        const uint32_t lm1[1] = {t0 == 2 ? top[1] : (t0 == 3 ? top[2] : top[3])};
+        const uint32_t lm2[1] = {t0 == 2 ? top[2] : (t0 == 3 ? top[3] : top[4])};
+        const int c1 = (kk + t0 - 1) / t0, c2 = (kk + t0) / (t0 + 1);
+        uint32_t b1 = 0u, b2 = 0u;
+#pragma unroll
+        for (int bit = 31; bit > 14; bit -= 2) {
+          (void)search2(lm1, c1, bit - 1, b1);
+          (void)search2(lm2, c2, bit - 1, b2);
+        }
+        const uint32_t l0 = b1 > b2 ? b1 : b2;
+        const uint32_t thr = uniform(l0 > 1u ? l0 : 1u);  // absent entries (key 0) never survive
+        uint2* surv = s_surv[wave];
+        int nsurv = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {  // survivors in vocabulary order, as in the narrow path
+          const bool sv = key[j] >= thr;
+          const unsigned long long m = __ballot(sv);
+          const int pos = nsurv + lanes_below(m);
+          const int dummy = kWideSurvCap + lane;
+          surv[sv ? min(pos, dummy) : dummy] = make_uint2(key[j], (uint32_t)idx[j]);
+          nsurv += __popcll(m);
+        }
+        if (nsurv <= kWideSurvCap) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          uint32_t sk[kWideSlots];
+          int si[kWideSlots];
+#pragma unroll
+          for (int j = 0; j < kWideSlots; ++j) {
+            const int q = j * kWave + lane;
+            const uint2 e = surv[q < nsurv ? q : kWideSurvCap + lane];
+            sk[j] = q < nsurv ? e.x : 0u;
+            si[j] = q < nsurv ? (int)e.y : -1;
+          }
+          sample_wide(p, row, sk, si, kk, thr, kmax, T, u, started, s_hist[wave]);
+          return;
+        }
+      }
+    }
+    sample_wide(p, row, key, idx, kk, 0u, kmax, T, u, started, s_hist[wave]);
     return;
   }
   // L0: the kk-th largest lane maximum, to its 10 leading bits (a lower bound on

@@ -1,7 +1,8 @@
 """GPU parity of the widened sampler (dec_sample_topk_ex) against the oracle, through the C ABI.
 
-* top_k > 64 (whole-row radix search; the CDF is one 64-lane scan per slot of 64 vocabulary
-  entries plus a running total): top-k sets exact; tokens exact except rows whose uniform
+* top_k > 64 (radix search over the row, or, for top_k <= 256, over the entries that pass a
+  lower bound on the k-th key, compacted in vocabulary order; the CDF is one 64-lane scan per
+  slot of 64 entries plus a running total): top-k sets exact; tokens exact except rows whose uniform
   lies within 1e-6 of an oracle CDF boundary; probabilities and their running sums within
   2e-6.  The 2e-6 comes from the arithmetic: the normaliser is a float32 sum with at most
   6 (tree) + ceil(V / 64) (running adds) roundings, 24 at V = 1089, so its relative error
@@ -191,3 +192,22 @@ def test_wide_nonfinite_logits_still_give_a_valid_index():
     tokens, idx, _ = _run(_dev(lg), dec.DEC_F32, B, V, 1096, T, k, u)
     assert np.all((tokens >= 0) & (tokens < V))
     assert np.all((idx >= 0) & (idx < V))
+
+
+@pytest.mark.parametrize("V,k", [(1089, 65), (1089, 200), (4096, 128), (4096, 256)])
+def test_wide_pruned_rows_with_heavy_ties(V, k):
+    # top_k in the pruned range: values on a few levels, so many entries tie at the k-th
+    # key (all survive the bound; the lowest indices are kept), and flat rows whose
+    # survivors overflow the pruned capacity (the whole row is searched instead)
+    B = 4
+    rng = np.random.default_rng(V + k)
+    S = V + (-V) % 8
+    lg = np.full((B, 9, S), 1e30, np.float32)
+    lg[:, :, :V] = np.round(rng.standard_normal((B, 9, V)) * 1.5).astype(np.float32)
+    lg[3, :4, :V] = 0.5                      # flat rows
+    lg[3, 4:, :V] = np.round(rng.random((5, V)) * 2).astype(np.float32)   # three levels
+    T = np.array([1.0, 0.6, 0.0, 1.4], np.float32)
+    u = rng.random((B, 9), dtype=np.float32)
+    print(f"[wide pruned ties] V={V} k={k}", flush=True)
+    got = _run(_dev(lg), dec.DEC_F32, B, V, S, T, k, u, fill=1089)
+    _compare(lg, V, T, k, u, None, 1089, got, WIDE_BAR)
