@@ -683,15 +683,16 @@ namespace {
 // fields are relaxed atomics: every writer stores the same value.
 struct DevInfo {
   std::atomic<int> cus{0};
-  std::atomic<int> occ[2][2][4] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
+  std::atomic<int> occ[2][2][5] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
 };
 DevInfo g_dev[64];
 
 // variant: 0 static, 1 paged, 2 widened (key masks / bf16 outputs, static caches), 3 static
-// with the current token's rows appended
+// with the current token's rows appended, 4 widened with a paged self cache
 template <typename T, int HD>
 void* attn_kernel_ptr(int variant) {
-  return variant == 3   ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD, true>)
+  return variant == 4   ? reinterpret_cast<void*>(&attn_decode_kernel<T, true, true, HD>)
+         : variant == 3 ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD, true>)
          : variant == 2 ? reinterpret_cast<void*>(&attn_decode_kernel<T, false, true, HD>)
          : variant == 1 ? reinterpret_cast<void*>(&attn_decode_kernel<T, true, false, HD>)
                         : reinterpret_cast<void*>(&attn_decode_kernel<T, false, false, HD>);
@@ -699,7 +700,10 @@ void* attn_kernel_ptr(int variant) {
 
 template <typename T, int HD>
 void attn_kernel_go(int variant, int blocks, size_t lds, hipStream_t stream, const AttnParams& p) {
-  if (variant == 3)
+  if (variant == 4)
+    hipLaunchKernelGGL((attn_decode_kernel<T, true, true, HD>), dim3(blocks), dim3(kAttnThreads),
+                       lds, stream, p);
+  else if (variant == 3)
     hipLaunchKernelGGL((attn_decode_kernel<T, false, false, HD, true>), dim3(blocks),
                        dim3(kAttnThreads), lds, stream, p);
   else if (variant == 2)
@@ -729,7 +733,7 @@ hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_
   const bool ex = p.seg[0].mask != nullptr || p.seg[0].out_bf16 ||
                   (p.nseg > 1 && (p.seg[1].mask != nullptr || p.seg[1].out_bf16));
   const bool app = p.seg[0].k_new != nullptr;  // static, plain: the ABI allows no other
-  const int variant = ex ? 2 : paged ? 1 : app ? 3 : 0;
+  const int variant = ex ? (paged ? 4 : 2) : paged ? 1 : app ? 3 : 0;
   const int wide = p.hd == kAttnHeadDimWide ? 1 : 0;
   if (!wide && p.hd != kAttnHeadDim) return hipErrorInvalidValue;
   void* fn = dtype == 0 ? (wide ? attn_kernel_ptr<uint16_t, kAttnHeadDimWide>(variant)

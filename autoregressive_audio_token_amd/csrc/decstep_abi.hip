@@ -316,6 +316,31 @@ int dec_attn_step_paged(const void* q_self, const void* k_pool, const void* v_po
                      reinterpret_cast<hipStream_t>(stream));
 }
 
+int dec_attn_step_paged_ex(const void* q_self, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* len, int block_size,
+                           int n_blocks, int max_blocks, void* out_self, const void* q_cross,
+                           const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                           const uint32_t* cross_mask, int mask_words, int L_cap_cross,
+                           void* out_cross, int n_layers, int B, int H, int hd, int dtype,
+                           int out_dtype, float scale, void* workspace, size_t ws_bytes,
+                           dec_stream_t stream) {
+  if (!block_table) return DEC_E_NULL;
+  if (out_dtype != DEC_BF16 && out_dtype != DEC_F32) return DEC_E_DTYPE;
+  if (max_blocks < 1 || block_size < 1 || (long long)max_blocks * block_size > (1LL << 30))
+    return DEC_E_SHAPE;
+  SegArgs s[2] = {{q_self, k_pool, v_pool, len, out_self, max_blocks * block_size},
+                  {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  s[0].table = block_table;
+  s[0].table_stride = max_blocks;
+  s[0].n_blocks = n_blocks;
+  s[0].block_size = block_size;
+  s[1].mask = cross_mask;
+  s[1].mask_words = mask_words;
+  s[0].out_bf16 = s[1].out_bf16 = out_dtype == DEC_BF16 ? 1 : 0;
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
 int dec_sample_topk(const float* logits, int B, int n_cb, int V_valid, int V_stride,
                     const float* temperature, int top_k, const float* uniforms,
                     const int32_t* step, int32_t fill_token, int32_t* tokens, int32_t* topk_idx,

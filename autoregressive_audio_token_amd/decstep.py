@@ -61,6 +61,8 @@ _SIGS = {
                                  _P, _SZ, _P]),
     "dec_attn_step_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P,
                                  _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "dec_attn_step_paged_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I,
+                                    _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "dec_sample_topk": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _P, ctypes.c_int32, _P, _P, _P,
                              _P]),
     "dec_sample_topk_philox": (_I, [_P, _I, _I, _I, _I, _P, _I, ctypes.c_uint64, _P,
@@ -193,6 +195,19 @@ def dec_attn_self_paged(q, k_pool, v_pool, block_table, len, out, n_layers, B, H
                                     _ptr(len), _ptr(out), n_layers, B, H, hd, block_size,
                                     n_blocks, max_blocks, dtype, scale, _ptr(workspace),
                                     ws_bytes, _stream(stream)))
+
+
+def dec_attn_step_paged_ex(q_self, k_pool, v_pool, block_table, len, block_size, n_blocks,
+                           max_blocks, out_self, q_cross, k_cross, v_cross, enc_len, cross_mask,
+                           mask_words, L_cap_cross, out_cross, n_layers, B, H, hd, dtype,
+                           out_dtype, scale, workspace, ws_bytes, stream=None):
+    _check(_lib.dec_attn_step_paged_ex(_ptr(q_self), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_table), _ptr(len), block_size, n_blocks,
+                                       max_blocks, _ptr(out_self), _ptr(q_cross),
+                                       _ptr(k_cross), _ptr(v_cross), _ptr(enc_len),
+                                       _ptr(cross_mask), mask_words, L_cap_cross,
+                                       _ptr(out_cross), n_layers, B, H, hd, dtype, out_dtype,
+                                       scale, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dec_attn_step_paged(q_self, k_pool, v_pool, block_table, len, block_size, n_blocks,

@@ -510,9 +510,6 @@ def main(argv=None):
     top_k = a.top_k if a.top_k > 0 else w.top_k
     ex_attn = a.cross_mask > 0 or a.out_bf16
     ex_samp = top_k > 64 or a.logits_bf16
-    if ex_attn and a.paged:
-        print("--cross-mask / --out-bf16 go with the static caches, not --paged", file=sys.stderr)
-        return 2
     model = a.schedule == "model"
     if model and (ex_attn or a.paged):
         print("--schedule model goes with the static caches and fp32 outputs", file=sys.stderr)
@@ -586,6 +583,15 @@ def main(argv=None):
         torch.cuda.synchronize()
 
     def attn(st, s):
+        if ex_attn and a.paged:          # a paged self cache with the widenings
+            dec.dec_attn_step_paged_ex(d["q_self"], st["k_self"], st["v_self"], table, d["len"],
+                                       a.paged, n_blocks, w.self_cap // a.paged, o_s,
+                                       d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"],
+                                       mask_d, mask_words, w.cross_cap, o_c, w.n_layers, w.batch,
+                                       w.heads, w.head_dim, code,
+                                       dec.DEC_BF16 if a.out_bf16 else dec.DEC_F32, w.scale, ws,
+                                       nb, s)
+            return
         if model:                        # one self and one cross launch per layer
             for l in range(w.n_layers):
                 dec.dec_attn_self(d["q_self"][l], st["k_self"][l], st["v_self"][l], d["len"],
@@ -729,6 +735,7 @@ def main(argv=None):
     if model:
         traffic_rec, traffic_why = None, "counters describe the stacked launch only"
     attn_entry = ("dec_attn_self + dec_attn_cross per layer" if model else
+                  "dec_attn_step_paged_ex" if ex_attn and a.paged else
                   "dec_attn_step_ex" if ex_attn else
                   "dec_attn_step_paged" if a.paged else "dec_attn_step")
     attn_launches = 2 * w.n_layers if model else 1

@@ -205,6 +205,20 @@ int dec_attn_step_paged(const void* q_self, const void* k_pool, const void* v_po
                         int dtype, float scale, void* workspace, size_t ws_bytes,
                         dec_stream_t stream);
 
+/* dec_attn_step_paged with the widenings of dec_attn_step_ex: a boolean key
+ * mask over the (static) description cache and fp32 or bf16 outputs, in one
+ * launch.  The self cache is paged as in dec_attn_self_paged (it takes no
+ * mask); cross_mask, mask_words and out_dtype as in dec_attn_step_ex.  With
+ * the same keys, lengths and mask, outputs equal dec_attn_step_ex's bit for bit. */
+int dec_attn_step_paged_ex(const void* q_self, const void* k_pool, const void* v_pool,
+                           const int32_t* block_table, const int32_t* len, int block_size,
+                           int n_blocks, int max_blocks, void* out_self, const void* q_cross,
+                           const void* k_cross, const void* v_cross, const int32_t* enc_len,
+                           const uint32_t* cross_mask, int mask_words, int L_cap_cross,
+                           void* out_cross, int n_layers, int B, int H, int hd, int dtype,
+                           int out_dtype, float scale, void* workspace, size_t ws_bytes,
+                           dec_stream_t stream);
+
 /* Fused temperature / top-k / softmax / sampling of the next token of every
  * codebook, with the codebook delay mask ("Future work", item 2: one kernel in
  * place of the temperature, top-k and softmax kernels; "Analysis and

@@ -300,6 +300,17 @@ def test_widened_sampler_host_validation():
 
 
 @_no_gpu
+def test_paged_widened_step_host_validation():
+    def call(tab=A, od=0, mask_words=16, **kw):
+        return D.raw_status("dec_attn_step_paged_ex", A, A, A, tab, A, 64, 100, 64, A, A, A, A,
+                            A, A, mask_words, 1024, A, 24, 1, 16, 64, 0, od,
+                            ctypes.c_float(0.125), A, 1 << 30, None)
+    assert call(tab=None) == D.DEC_E_NULL
+    assert call(od=5) == D.DEC_E_DTYPE
+    assert call(mask_words=15) == D.DEC_E_SHAPE      # 2 words per 64 keys, an even count
+
+
+@_no_gpu
 def test_fused_append_host_validation():
     def call(kn=A, vn=A, **kw):
         a = dict(q=A, len=A, out=A)

@@ -44,10 +44,10 @@ def test_unknown_workload_has_no_traffic():
     assert rec is None and "no counter summary" in why
 
 
-def test_widened_attention_with_paged_cache_is_refused():
-    # key masks and bf16 outputs go with the static caches; refused before any GPU work
-    assert bench.main(["--paged", "64", "--cross-mask", "0.5"]) == 2
-    assert bench.main(["--paged", "64", "--out-bf16"]) == 2
+def test_paged_and_widened_options_combine():
+    # a paged self cache with a description mask and bf16 outputs: dec_attn_step_paged_ex
+    a = bench.parse(["--paged", "64", "--cross-mask", "0.5", "--out-bf16"])
+    assert (a.paged, a.cross_mask, a.out_bf16) == (64, 0.5, True)
 
 
 def test_variant_options_parse():

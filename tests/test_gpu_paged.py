@@ -136,3 +136,49 @@ def test_out_of_pool_table_entry_reads_zero_rows():
                 V[blk * bs:(blk + 1) * bs] = 0.0
             o = oattn.attend_one(q[layer, 0, h], K, V, n, w.scale)
             assert hp.row_rel_err(got[layer, 0, h], o) <= BAR
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_paged_widened_step_equals_static_widened_step(out, split, monkeypatch):
+    # a paged self cache with a masked description and fp32 / bf16 outputs in one launch
+    # (dec_attn_step_paged_ex) against the static widened step on the same keys
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    w = dataclasses.replace(_workload(2), cross_cap=512, cross_len=None, cross_len_range=(1, 512))
+    lens = [1500, 300]
+    enc = np.array([512, 300], np.int32)
+    print(f"[paged ex] out={out} split={split}", flush=True)
+    d = wdev.step_inputs(w, hp.DEV, self_lens=lens, cross_lens=enc,
+                         fill_lens=(np.array(lens), np.full(2, w.cross_cap)))
+    lens_d = _dev(np.array(lens, np.int32))
+    rng = np.random.default_rng(5)
+    mask = rng.random((2, w.cross_cap)) < 0.4
+    mask[:, 64:192] = False                   # whole tiles with no attended key
+    words = 2 * ((w.cross_cap + 63) // 64)
+    packed = np.zeros((2, words), np.uint32)
+    for j in range(w.cross_cap):
+        packed[:, j // 32] |= mask[:, j].astype(np.uint32) << np.uint32(j % 32)
+    mask_d = _dev(packed)
+    ws = hp.workspace(w, w.self_cap, w.cross_cap)
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    ocode = dec.DEC_BF16 if out == "bf16" else dec.DEC_F32
+    shape = (w.n_layers, 2, w.heads, 64)
+    r_s, r_c = torch.empty(shape, dtype=odt, device=hp.DEV), torch.empty(shape, dtype=odt, device=hp.DEV)
+    dec.dec_attn_step_ex(d["q_self"], d["k_self"], d["v_self"], lens_d, w.self_cap, r_s,
+                         d["q_cross"], d["k_cross"], d["v_cross"], d["enc_len"], mask_d, words,
+                         w.cross_cap, r_c, w.n_layers, 2, w.heads, 64, dec.DEC_BF16, ocode,
+                         w.scale, ws[0], ws[1])
+    bs = 128
+    kp, table = _paged(gen.cache(w, "self", "k", lens), lens, bs, 3, seed=9)
+    vp, _ = _paged(gen.cache(w, "self", "v", lens), lens, bs, 3, seed=9)
+    p_s, p_c = torch.empty_like(r_s), torch.empty_like(r_c)
+    dec.dec_attn_step_paged_ex(d["q_self"], _dev(kp), _dev(vp), _dev(table), lens_d, bs,
+                               kp.shape[1], w.self_cap // bs, p_s, d["q_cross"], d["k_cross"],
+                               d["v_cross"], d["enc_len"], mask_d, words, w.cross_cap, p_c,
+                               w.n_layers, 2, w.heads, 64, dec.DEC_BF16, ocode, w.scale,
+                               ws[0], ws[1])
+    torch.cuda.synchronize()
+    for a, b in ((p_s, r_s), (p_c, r_c)):
+        va = a.view(torch.int16) if out == "bf16" else a.view(torch.int32)
+        vb = b.view(torch.int16) if out == "bf16" else b.view(torch.int32)
+        assert torch.equal(va, vb)
