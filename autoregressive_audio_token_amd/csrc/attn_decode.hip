@@ -150,10 +150,10 @@ __device__ __forceinline__ int nchunks(int n, int clog) {
   return n > 0 ? ((n - 1) >> clog) + 1 : 0;
 }
 
-// Work items per (layer, head) of a sequence with n valid keys.
-__device__ __forceinline__ int items_per_lh(int n, int cpi, int clog) {
+// Work items per (layer, head) of a sequence with n valid keys (1 << cpi_log2 chunks each).
+__device__ __forceinline__ int items_per_lh(int n, int cpi_log2, int clog) {
   const int c = nchunks(n, clog);
-  return c > cpi ? (c + cpi - 1) / cpi : 1;
+  return c > (1 << cpi_log2) ? ((c - 1) >> cpi_log2) + 1 : 1;
 }
 
 // Waves that share one sequence: the smallest power of two covering n keys in one
@@ -169,13 +169,13 @@ __device__ __forceinline__ int waves_per_seq(int n) {
 
 // Work items of a (segment, b) group with n valid keys.
 template <int HD>
-__device__ __forceinline__ int group_items(int n, int NLH, int cpi, int clog) {
-  const int S = waves_per_seq<HD>(n);
+__device__ __forceinline__ int group_items(int n, int NLH, int cpi_log2, int clog) {
+  const int S = waves_per_seq<HD>(n);  // a power of two
   if (S < kAttnWaves) {
-    const int P = kAttnWaves / S;
-    return (NLH + P - 1) / P;
+    const int pl = __builtin_ctz(kAttnWaves) - __builtin_ctz(S);  // log2(sequences per item)
+    return (NLH + (1 << pl) - 1) >> pl;
   }
-  return NLH * items_per_lh(n, cpi, clog);
+  return NLH * items_per_lh(n, cpi_log2, clog);
 }
 
 // Fold chunk state (mc, lc, ac) into the running state (m, l, a); the first
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
   const int B = p.B;
   const int G = p.nseg * B;
   const int NLH = p.NL * p.H;
-  const int cpi = p.cpi;
+  const int cpl = p.cpi_log2;      // chunks per work item: 1 << cpl
   const int clog = p.chunk_log2;  // keys per chunk: 1 << clog, whole tile rounds
   int* s_n = s_dyn;
   int* s_order = s_dyn + G;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
       const int cap = cross ? p.seg[1].L_cap : p.seg[0].L_cap;
       n = len[cross ? lane - B : lane];
       n = n < 0 ? 0 : (n > cap ? cap : n);
-      items = group_items<HD>(n, NLH, cpi, clog);
+      items = group_items<HD>(n, NLH, cpl, clog);
     }
     int rank = 0;  // stable rank by descending length
     for (int j = 0; j < G; ++j) {
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const int lo = min(G, tid * per);
     const int hi = min(G, lo + per);
     int local = 0;
-    for (int i = lo; i < hi; ++i) local += group_items<HD>(s_n[s_order[i]], NLH, cpi, clog);
+    for (int i = lo; i < hi; ++i) local += group_items<HD>(s_n[s_order[i]], NLH, cpl, clog);
     int ex = wave_inclusive_sum_int(local, lane) - local;
     if (lane == kWave - 1) s_wsum[wave] = ex + local;
     __syncthreads();
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     }
     for (int i = lo; i < hi; ++i) {
       s_pref[i] = ex;
-      ex += group_items<HD>(s_n[s_order[i]], NLH, cpi, clog);
+      ex += group_items<HD>(s_n[s_order[i]], NLH, cpl, clog);
     }
     if (tid == 0) s_pref[G] = total;
     __syncthreads();
@@ -438,31 +438,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const AttnSeg& S = cross ? p.seg[1] : p.seg[0];
     const int b = cross ? g - B : g;
     const int nck = nchunks(n, clog);
-    const int spw = waves_per_seq<HD>(n);        // waves per sequence
+    const int spw = waves_per_seq<HD>(n);        // waves per sequence, a power of two
+    const int spw_l = __builtin_ctz(spw);
     const bool packed = spw < kAttnWaves;        // several sequences share this item
-    const int P = kAttnWaves / spw;              // sequences in this item (packed)
+    const int P = kAttnWaves >> spw_l;           // sequences in this item (packed)
 
-    // this wave's sequence and its first key within each chunk
+    // this wave's sequence and its first key within each chunk.  Unpacked items of a group
+    // run chunk-major: item r holds chunk group r / NLH of (layer, head) r % NLH.
     int wave_lh, wave_part, c0, c1;
     bool whole;
     if (packed) {  // one tile per wave, one chunk
-      wave_lh = r * P + wave / spw;
-      wave_part = wave % spw;
+      wave_lh = r * P + (wave >> spw_l);
+      wave_part = wave & (spw - 1);
       c0 = 0;
       c1 = nck;
       whole = true;
     } else {
-      const int ipl = items_per_lh(n, cpi, clog);
-      const int k = r % ipl;
-      wave_lh = r / ipl;
+      const int ipl = items_per_lh(n, cpl, clog);
+      const int k = ipl == 1 ? 0 : (int)udiv((uint32_t)r, p.div_nlh);
+      wave_lh = r - k * NLH;
       wave_part = wave;
-      c0 = k * cpi;
-      c1 = min(nck, c0 + cpi);
+      c0 = k << cpl;
+      c1 = min(nck, c0 + (1 << cpl));
       whole = ipl == 1;
     }
     const bool wave_ok = wave_lh < NLH;  // the last packed item may have empty slots
     const int wlh = wave_ok ? wave_lh : 0;
-    const size_t wave_sidx = ((size_t)(wlh / p.H) * B + b) * p.H + (wlh % p.H);
+    const int wl = (int)udiv((uint32_t)wlh, p.div_h);  // layer, and head wlh - wl * H
+    const int wh = wlh - wl * p.H;
+    const size_t wave_sidx = ((size_t)wl * B + b) * p.H + wh;
 
     // the combining threads: sequence slot `slot`, head dimension `d`
     const int slot = tid / HD;
@@ -471,7 +475,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const int slot_lh = packed ? r * P + slot : wave_lh;
     const bool slot_ok = slot < nslot && slot_lh < NLH;
     const int slh = slot_ok ? slot_lh : 0;
-    const size_t slot_sidx = ((size_t)(slh / p.H) * B + b) * p.H + (slh % p.H);
+    const int sl = (int)udiv((uint32_t)slh, p.div_h);
+    const size_t slot_sidx = ((size_t)sl * B + b) * p.H + (slh - sl * p.H);
 
     if (n == 0) {  // no valid key: defined output of zeros
       if (slot_ok) {
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
     const T* vp = static_cast<const T*>(S.v);
     size_t head_off = 0;  // paged: offset of (layer, head) inside a block, before the block term
     if (paged) {
-      head_off = (size_t)(wlh / p.H) * S.n_blocks;  // layer's first block
+      head_off = (size_t)wl * S.n_blocks;  // layer's first block
     } else {
       kp += wave_sidx * (size_t)S.L_cap * HD;
       vp += wave_sidx * (size_t)S.L_cap * HD;
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_decode_kernel(AttnParams p)
           // rows of this tile inside its block; none past n or for an entry outside the pool
           int rows = base < n ? min(bs - row, n - base) : 0;
           if (blk < 0 || blk >= S.n_blocks) rows = 0;
-          const size_t off = (((head_off + (size_t)(unsigned)blk) * p.H + (wlh % p.H)) * bs + row) * HD;
+          const size_t off = (((head_off + (size_t)(unsigned)blk) * p.H + wh) * bs + row) * HD;
           return {rows_rsrc(kp + off, rows, kRowBytes), rows_rsrc(vp + off, rows, kRowBytes), 0,
                   keep};
         };
@@ -765,6 +770,10 @@ hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_
   }
   for (int s = 0; s < 2; ++s)
     p.seg[s].nck_cap = p.seg[s].L_cap > 0 ? ((p.seg[s].L_cap - 1) >> p.chunk_log2) + 1 : 0;
+  if (p.cpi < 1 || (p.cpi & (p.cpi - 1)) != 0) return hipErrorInvalidValue;
+  p.cpi_log2 = attn_log2(p.cpi);
+  p.div_nlh = div_magic((uint32_t)(p.NL * p.H));
+  p.div_h = div_magic((uint32_t)p.H);
   if (blocks <= 0) {
     hipError_t e = hipSuccess;
     DevInfo& di = g_dev[dev & 63];

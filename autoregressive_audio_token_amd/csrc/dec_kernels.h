@@ -50,6 +50,29 @@ constexpr int kAttnSortMax = 1024;                  // groups ordered longest-fi
 constexpr int kAttnSplitBelow = 512;                // below this many sequences per launch, every
                                                     // chunk is its own work item (balance)
 
+// Division by a launch constant d >= 1, exact for every 32-bit x: a multiply-high, an add
+// and two shifts (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994; the case whose multiplier needs 33 bits, applied as
+// t + ((x - t) >> 1)).  Keeps runtime integer divisions off the work-item decode.
+struct DivMagic {
+  uint32_t m;
+  int s1, s2;
+};
+inline DivMagic div_magic(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;  // 2^(l-1) < d <= 2^l
+  DivMagic r;
+  r.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  r.s1 = l < 1 ? l : 1;
+  r.s2 = l > 1 ? l - 1 : 0;
+  return r;
+}
+__device__ __forceinline__ uint32_t udiv(uint32_t x, const DivMagic& d) {
+  const uint32_t t = __umulhi(x, d.m);
+  return (t + ((x - t) >> d.s1)) >> d.s2;
+}
+static_assert((kAttnWaves & (kAttnWaves - 1)) == 0, "waves per workgroup: a power of two");
+
 // One attention problem ("segment"): self-attention or cross-attention of a step.
 struct AttnSeg {
   const void* q;          // [NL, B, H, hd]
@@ -82,7 +105,10 @@ struct AttnParams {
   int nseg;
   int NL, B, H;
   int hd;                 // 64 or 128 (selects the instantiation)
-  int cpi;                // chunks per work item (>= nck_cap of every segment: no split)
+  int cpi;                // chunks per work item (>= nck_cap of every segment: no split),
+                          // a power of two
+  int cpi_log2;           // log2(cpi), set by the launcher
+  DivMagic div_nlh, div_h;  // division by NL * H and by H, set by the launcher
   int chunk_log2;         // log2(keys per chunk); 0: the launcher chooses
   int min_chunk_log2;     // the smallest chunk the workspace holds partials for
   float qscale;           // scale * log2(e): scores are formed in base 2
