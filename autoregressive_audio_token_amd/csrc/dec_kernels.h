@@ -58,10 +58,10 @@ struct DivMagic {
   uint32_t m;
   int s1, s2;
 };
-inline DivMagic div_magic(uint32_t d) {
+constexpr DivMagic div_magic(uint32_t d) {
   int l = 0;
   while ((1ull << l) < d) ++l;  // 2^(l-1) < d <= 2^l
-  DivMagic r;
+  DivMagic r{};
   r.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
   r.s1 = l < 1 ? l : 1;
   r.s2 = l > 1 ? l - 1 : 0;
@@ -71,6 +71,23 @@ __device__ __forceinline__ uint32_t udiv(uint32_t x, const DivMagic& d) {
   const uint32_t t = __umulhi(x, d.m);
   return (t + ((x - t) >> d.s1)) >> d.s2;
 }
+// The same arithmetic on the host, checked against division at compile time below.
+constexpr uint32_t udiv_host(uint32_t x, DivMagic d) {
+  const uint32_t t = (uint32_t)(((uint64_t)x * d.m) >> 32);
+  return (t + ((x - t) >> d.s1)) >> d.s2;
+}
+constexpr bool div_magic_ok(uint32_t d) {
+  const uint32_t xs[] = {0u, 1u, d - 1u, d, d + 1u, 2u * d - 1u, 2u * d, 12345u, 0x7FFFFFFFu,
+                         0x80000000u, 0xFFFFFFFEu, 0xFFFFFFFFu};
+  for (uint32_t x : xs)
+    if (udiv_host(x, div_magic(d)) != x / d) return false;
+  return true;
+}
+static_assert(div_magic_ok(1) && div_magic_ok(2) && div_magic_ok(3) && div_magic_ok(5) &&
+                  div_magic_ok(7) && div_magic_ok(16) && div_magic_ok(24) && div_magic_ok(384) &&
+                  div_magic_ok(1000) && div_magic_ok(4095) && div_magic_ok(65537) &&
+                  div_magic_ok(0x7FFFFFFFu) && div_magic_ok(0xFFFFFFFFu),
+              "multiply-high division agrees with division");
 static_assert((kAttnWaves & (kAttnWaves - 1)) == 0, "waves per workgroup: a power of two");
 
 // One attention problem ("segment"): self-attention or cross-attention of a step.
