@@ -664,17 +664,24 @@ def main(argv=None):
         dec.dec_graph_launch(graph, stream)
     stream.synchronize()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # one continuous timed region of `launches` graph replays; events at up to ten block
+    # boundaries inside it give per-block step times (their median is reported beside the
+    # total, which is what `value` is computed from)
+    n_blocks = min(10, launches)
+    bounds = [round(i * launches / n_blocks) for i in range(n_blocks + 1)]
+    evs_blk = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(launches):
-        dec.dec_graph_launch(graph, stream)
-    e1.record(stream)
+    evs_blk[0].record(stream)
+    for i in range(n_blocks):
+        for _ in range(bounds[i + 1] - bounds[i]):
+            dec.dec_graph_launch(graph, stream)
+        evs_blk[i + 1].record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / steps
+    ms_per_step = evs_blk[0].elapsed_time(evs_blk[-1]) / steps
+    blk_us = sorted(evs_blk[i].elapsed_time(evs_blk[i + 1]) * 1e3 / ((bounds[i + 1] - bounds[i]) * R)
+                    for i in range(n_blocks))
     out_ok = bool(torch.isfinite(o_s).all().item() and torch.isfinite(o_c).all().item())
     tok_h = tok.cpu().numpy()
     tok_ok = bool(np.all((tok_h >= 0) & (tok_h < w.vocab_valid) | (tok_h == w.fill_token)))
@@ -750,6 +757,8 @@ def main(argv=None):
         "warmup": warm * R,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_blocks": {"blocks": n_blocks, "median": round(blk_us[len(blk_us) // 2], 3),
+                               "min": round(blk_us[0], 3), "max": round(blk_us[-1], 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
