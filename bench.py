@@ -18,6 +18,7 @@ import json
 import math
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -433,6 +434,17 @@ def copy_calibration(mib):
     return 0 if ok else 1
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, seconds):
     """The oracle, as it stands, on whole decode steps of the same workload."""
     import numpy as np
@@ -453,34 +465,39 @@ def cpu_baseline(w, seconds):
     lg, u, T = gen.logits(w), gen.uniforms(w), gen.temperatures(w)
     dec16 = oattn.bf16_bits_to_f64 if w.dtype == "bf16" else (lambda x: x.astype(np.float64))
 
+    tasks = [(kind, layer, b) for kind in ("self", "cross") for layer in range(w.n_layers)
+             for b in range(w.batch)]
+
+    def attend(task):  # every head of one (segment, layer, sequence)
+        kind, layer, b = task
+        K, V = rows[task]
+        n = int(lens[kind][b])
+        for h in range(w.heads):
+            oattn.attend_one(dec16(q[kind][layer, b, h]), dec16(K[h]), dec16(V[h]), n, w.scale)
+
     def one_step():
-        for kind in ("self", "cross"):
-            for layer in range(w.n_layers):
-                for b in range(w.batch):
-                    K, V = rows[kind, layer, b]
-                    n = int(lens[kind][b])
-                    for h in range(w.heads):
-                        oattn.attend_one(dec16(q[kind][layer, b, h]), dec16(K[h]), dec16(V[h]),
-                                         n, w.scale)
+        for t in tasks:
+            attend(t)
         osamp.sample(lg, w.vocab_valid, T, w.top_k, u, None, w.fill_token)
 
-    with threadpool_limits(1):
-        steps, t0 = 0, time.perf_counter()
-        while True:
+    times, t0 = [], time.perf_counter()
+    with threadpool_limits(1):  # one thread, BLAS included
+        while len(times) < 10 or time.perf_counter() - t0 < seconds:
+            s = time.perf_counter()
             one_step()
-            steps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
+            times.append(time.perf_counter() - s)
     valid = configs.valid_kv_bytes(w, s_len, c_len)
-    return {"value": round(valid * steps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+    med = statistics.median(times)
+    return {"value": round(valid / med / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{steps} whole decode steps of {w.name} (all layers, self+cross "
+            "sample": f"{len(times)} whole decode steps of {w.name} (all layers, self+cross "
                       f"attention over the valid prefixes, then the sampler), float64 NumPy, "
-                      f"one thread",
-            "us_per_step": round(el / steps * 1e6, 1),
-            "host_cpu": platform.processor() or platform.machine(),
-            "host_cores_visible": len(os.sched_getaffinity(0))}
+                      f"one thread; value from the median step time",
+            "us_per_step": round(med * 1e6, 1),
+            "us_per_step_mean": round(sum(times) / len(times) * 1e6, 1),
+            "host_cpu": _cpu_model(),
+            "host_cores_visible": len(os.sched_getaffinity(0)),
+            "host_cpu_count": os.cpu_count()}
 
 
 def main(argv=None):
