@@ -70,3 +70,17 @@ def test_measurement_options_parse():
     a = bench.parse(["--schedule", "model", "--decode-loop", "--calibrate"])
     assert (a.schedule, a.decode_loop, a.calibrate) == ("model", True, True)
     assert bench.parse([]).schedule == "stacked"
+
+
+def test_oracle_baseline_reports_the_median_of_at_least_ten_steps():
+    from workloads import configs, gen
+    r = bench.cpu_baseline(configs.TINY, 0.0)
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
+    steps = int(r["sample"].split()[0])
+    assert steps >= 10
+    # value: the valid K/V bytes of one step over the median step time
+    s_len, c_len = gen.lengths(configs.TINY)
+    valid = configs.valid_kv_bytes(configs.TINY, s_len, c_len)
+    assert abs(r["value"] - valid / (r["us_per_step"] * 1e-6) / 1e9) <= 1e-3 * r["value"] + 1e-4
+    assert r["host_cores_visible"] >= 1 and r["host_cpu_count"] >= r["host_cores_visible"]
+    assert isinstance(r["host_cpu"], str) and r["host_cpu"]
