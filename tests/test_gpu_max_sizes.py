@@ -1,0 +1,78 @@
+"""GPU parity at the largest sequence the attention ABI accepts, through the C ABI.
+
+One sequence's cache must stay addressable with 32-bit byte offsets (its bytes plus 64 KiB,
+where loads that move no bytes are addressed, below 2^31): 16,776,703 keys of 128 bytes
+(bf16, head dim 64) or 4,194,175 keys of 512 bytes (fp32, head dim 128).  Every key of the
+cache is valid here, so the last tile is ragged and every chunk state is folded.
+
+Closed form instead of the fp64 oracle (which would need 8 GB per operand): with K = 0 every
+score is zero, the softmax weights are all equal and the output is the mean of the V rows.
+V[j, d] = (j + d) mod 7, exact in both dtypes, with a mean over n rows of
+(21 m + sum_{t < r} (t + d) mod 7) / n for n = 7 m + r; rows 0, n / 2 and n - 1 hold 2^20
+instead, so that a missing first, middle or last row moves the mean by about 2%.  Bar: 2e-3
+relative (max-norm), as everywhere; the fp32 sums of integers stay far below it.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import autoregressive_audio_token_amd as dec  # noqa: E402
+from tests import hip_path as hp  # noqa: E402
+
+BAR = 2e-3
+
+
+def _largest_cap(hd, elem_bytes):
+    return (0x7FFFFFFF - 65536) // (hd * elem_bytes)
+
+
+SPIKE = 2.0 ** 20
+
+
+def _spike_rows(n):
+    return (0, n // 2, n - 1)
+
+
+def _mean_pattern(n, hd):
+    m, r = divmod(n, 7)
+    out = []
+    for d in range(hd):
+        total = 21 * m + sum((t + d) % 7 for t in range(r))
+        total += sum(SPIKE - (j + d) % 7 for j in _spike_rows(n))
+        out.append(total / n)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("dtype,hd", [("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("split", ["1", "0"])
+def test_largest_accepted_sequence(dtype, hd, split, monkeypatch):
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    tdt, code, eb = ((torch.bfloat16, dec.DEC_BF16, 2) if dtype == "bf16"
+                     else (torch.float32, dec.DEC_F32, 4))
+    cap = _largest_cap(hd, eb)
+    print(f"[max size] dtype={dtype} hd={hd} cap={cap} split={split}", flush=True)
+    assert cap * hd * eb + 65536 <= 0x7FFFFFFF < (cap + 1) * hd * eb + 65536
+    pattern = ((torch.arange(7, device=hp.DEV)[:, None] + torch.arange(hd, device=hp.DEV)[None, :])
+               % 7).to(tdt)
+    v = pattern.repeat((cap + 6) // 7, 1)[:cap].reshape(1, 1, 1, cap, hd).contiguous()
+    for j in _spike_rows(cap):
+        v[0, 0, 0, j, :] = SPIKE
+    k = torch.zeros_like(v)
+    q = torch.randn((1, 1, 1, hd), device=hp.DEV).to(tdt)
+    lens = torch.tensor([cap], dtype=torch.int32, device=hp.DEV)
+    out = torch.full((1, 1, 1, hd), float("nan"), dtype=torch.float32, device=hp.DEV)
+    nb = dec.dec_attn_workspace_bytes(1, 1, 1, hd, cap, 0)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=hp.DEV)
+    dec.dec_attn_workspace_init(ws, nb)
+    dec.dec_attn_self(q, k, v, lens, out, 1, 1, 1, cap, hd, code, hd ** -0.5, ws, nb)
+    got = hp.host(out).reshape(hd).astype(np.float64)
+    want = _mean_pattern(cap, hd)
+    err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+    print(f"  max_rel_err={err:.3e}", flush=True)
+    assert err <= BAR
+    # one key more is refused on the host, before any launch
+    with pytest.raises(dec.DecError) as e:
+        dec.dec_attn_self(q, k, v, lens, out, 1, 1, 1, cap + 1, hd, code, hd ** -0.5, ws, nb)
+    assert e.value.status == dec.DEC_E_UNSUPPORTED
