@@ -201,6 +201,43 @@ def test_split_and_whole_sequence_modes_agree_bitwise(n, chunk, monkeypatch):
     _check("self", w, d, torch.from_numpy(split), src, rows, np.array([n]))
 
 
+@pytest.mark.parametrize("B,entry", [(40, "step"), (100, "self"), (1100, "self"), (2048, "step")])
+def test_many_groups_take_the_lds_work_list(B, entry, monkeypatch):
+    # More than 64 (segment, sequence) groups: the work list is built in LDS and binary
+    # searched instead of in registers; above 1024 groups it stays in group order; 4096
+    # groups (the step at B = 2048) is the most one launch takes.  Random lengths with
+    # empty and full sequences; every sequence checked against the oracle on a sampled
+    # (layer, head), and the two schedules bit-equal at a fixed chunk.
+    import dataclasses
+    w = dataclasses.replace(configs.MINI_V1, n_layers=1, batch=B, heads=2, self_cap=320,
+                            cross_cap=96, self_len=None, cross_len=None,
+                            self_len_range=(1, 2), cross_len_range=(1, 2))
+    rng = np.random.default_rng(B)
+    s_len = rng.integers(0, w.self_cap + 1, B).astype(np.int32)
+    c_len = rng.integers(0, w.cross_cap + 1, B).astype(np.int32)
+    s_len[:3] = [0, 1, w.self_cap]
+    c_len[:3] = [w.cross_cap, 0, 33]
+    print(f"[many groups] B={B} entry={entry} groups={B * (2 if entry == 'step' else 1)}",
+          flush=True)
+    d = _inputs(w, self_lens=s_len, cross_lens=c_len)
+    ws = hp.workspace(w, w.self_cap, w.cross_cap)
+    src = RowSource(w, s_len, c_len)
+    rows = sampled_rows(w, B + 16, seed=B)
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "1024")
+    outs = {}
+    for split in ("0", "1"):
+        monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+        if entry == "step":
+            outs[split] = [hp.host(t) for t in hp.attn_step(w, d, ws)]
+        else:
+            outs[split] = [hp.host(hp.attn("self", w, d, ws=ws))]
+    for a, b in zip(outs["0"], outs["1"]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _check("self", w, d, torch.from_numpy(outs["0"][0]), src, rows, s_len)
+    if entry == "step":
+        _check("cross", w, d, torch.from_numpy(outs["0"][1]), src, rows, c_len)
+
+
 def test_per_layer_calls_equal_the_stacked_call_bitwise(monkeypatch):
     # the model-shaped schedule: one call per layer on offset pointers (a launch of
     # 16 sequences, which spreads chunks over workgroups) against one stacked launch.
