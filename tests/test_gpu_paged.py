@@ -53,7 +53,7 @@ def _static_out(w, d, lens_d, ws):
     return hp.attn("self", w, d, ws=ws, lens=lens_d)
 
 
-@pytest.mark.parametrize("bs", [64, 256])
+@pytest.mark.parametrize("bs", [64, 256, 4096])
 @pytest.mark.parametrize("split", ["1", "0"])
 def test_paged_self_equals_static_and_oracle(bs, split, monkeypatch):
     monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
