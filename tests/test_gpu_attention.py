@@ -292,10 +292,14 @@ def test_small_chunks_ragged_lengths(n, chunk, monkeypatch):
     _check("self", w, d, out, src, rows, lens)
 
 
-def test_split_combine_is_stable_over_many_back_to_back_runs():
-    # every chunk of every cross sequence is its own work item here; the last chunk
-    # of a sequence to arrive folds the others' published states.  Many unsynchronised
-    # launches must all produce the same bits, equal to the oracle within the bar.
+def test_split_combine_is_stable_over_many_back_to_back_runs(monkeypatch):
+    # every 256-key chunk of every sequence is its own work item here (split mode forced:
+    # left to choose, this 768-sequence launch keeps whole sequences); the last chunk of a
+    # description to arrive folds the other three chunks' published states.  Many
+    # unsynchronised launches must all produce the same bits, equal to the oracle within
+    # the bar.
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
+    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "256")
     w = configs.LONG_DESCRIPTION
     d = _inputs(w)
     ws = hp.workspace(w, w.self_cap, w.cross_cap)
