@@ -154,7 +154,11 @@ def test_fused_step_equals_separate_calls_and_runs_repeat_bitwise():
 
 
 @pytest.mark.parametrize("blocks", [1, 7, 256, 5000])
-def test_grid_size_changes_no_bit(blocks, monkeypatch):
+@pytest.mark.parametrize("split", ["0", "1"])
+def test_grid_size_changes_no_bit(blocks, split, monkeypatch):
+    # both schedules: in split mode a small grid walks many chunk items per workgroup,
+    # publishing each chunk state and folding a sequence when its last chunk arrives
+    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
     w = configs.MINI_V1
     d = _inputs(w, self_lens=[1500], cross_lens=[64])
     ref_s, ref_c = [hp.host(t) for t in hp.attn_step(w, d)]
