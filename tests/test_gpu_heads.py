@@ -68,6 +68,32 @@ def test_lm_head_every_mfma_tiling(B, D, cfg, monkeypatch):
     _check_lm_head(B, D, 2000 + B * 7 + D + cfg)
 
 
+@pytest.mark.parametrize("B", [1, 9])
+@pytest.mark.parametrize("path", ["default", "gemv"])
+def test_lm_head_large_vocabulary(B, path, monkeypatch):
+    # a text-sized vocabulary (50,257 rows, odd, so the last row group is partial): many row
+    # groups per codebook; padding columns untouched; the same relative bar
+    if path == "gemv":
+        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
+    n_cb, D, V = 2, 1024, 50257
+    S = V + (-V) % 8
+    print(f"[lm_head large V] B={B} V={V} path={path}", flush=True)
+    rng = np.random.default_rng(V + B)
+    h = _bf16(rng, (B, D), 1.0)
+    W = _bf16(rng, (n_cb, S, D), 1.0 / 32)
+    W[:, V:, :] = gen.BF16_NAN
+    logits = torch.full((B, n_cb, S), float(SENTINEL), dtype=torch.float32, device=hp.DEV)
+    dec.dec_lm_head(_dev(h), _dev(W), logits, B, D, n_cb, V, S)
+    got = hp.host(logits)
+    assert np.all(got[:, :, V:] == SENTINEL), "padding columns written"
+    want = oheads.lm_head(h, W, V)
+    hf = np.abs(oattn.bf16_bits_to_f64(h))
+    for c in range(n_cb):
+        absum = hf @ np.abs(oattn.bf16_bits_to_f64(W[c, :V])).T
+        err = np.abs(got[:, c, :V] - want[:, c])
+        assert np.all(err <= 2e-5 * absum), float(np.max(err / absum))
+
+
 @pytest.mark.parametrize("V", [1, 15, 16, 17, 1089])
 def test_lm_head_partial_row_groups_and_unaligned_output(V):
     # a last group of 16 rows that is partly past V_valid; an output pointer that is only
