@@ -161,3 +161,25 @@ def test_embed_sum_matches_oracle():
                 absum[b] += np.abs(Ef[c, toks[b, c]])
     assert np.all(np.abs(got - want) <= 1e-6 * absum)
     assert np.all(got[3] == 0.0)
+
+
+def test_embed_sum_at_the_largest_batch():
+    # B = 65535, the most the entry accepts (one workgroup row per sequence): every row
+    # against the oracle, tokens drawn from -1..V_emb (out-of-range entries add nothing)
+    n_cb, V_emb, D, B = 9, configs.VOCAB_PADDED, 1024, 65535
+    rng = np.random.default_rng(65535)
+    E = _bf16(rng, (n_cb, V_emb, D), 0.5)
+    toks = rng.integers(-1, V_emb + 1, (B, n_cb)).astype(np.int32)
+    print(f"[embed max B] B={B}", flush=True)
+    x = torch.full((B, D), float("nan"), dtype=torch.float32, device=hp.DEV)
+    dec.dec_embed_sum(_dev(toks), _dev(E), x, B, n_cb, V_emb, D)
+    got = hp.host(x)
+    want = oheads.embed(toks, E)
+    Ef = np.abs(oattn.bf16_bits_to_f64(E))
+    ok = (toks >= 0) & (toks < V_emb)
+    absum = np.zeros((B, D))
+    for c in range(n_cb):
+        absum += Ef[c, np.clip(toks[:, c], 0, V_emb - 1)] * ok[:, c:c + 1]
+    assert np.all(np.abs(got - want) <= 1e-6 * absum)
+    with pytest.raises(dec.DecError):
+        dec.dec_embed_sum(_dev(toks), _dev(E), x, B + 1, n_cb, V_emb, D)
