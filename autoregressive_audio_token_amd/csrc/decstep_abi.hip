@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "../../include/decstep.h"
 #include "dec_common.h"
 #include "dec_kernels.h"
@@ -54,6 +56,32 @@ WsLayout ws_layout(int NL, int B, int H, int hd, const int (&L_cap)[2], int chun
   return w;
 }
 
+// The no-allocation entry point's workspace: one array per GPU, of a fixed size, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address is taken with hipGetSymbolAddress, once per device,
+// and only that address is ever passed to kernels or fills.
+constexpr size_t kScratchBytes = DEC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's address of `scratch` (looked up on the first call on the device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // every thread finds the same
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
 bool hd_ok(int hd) { return hd == dec::kAttnHeadDim || hd == dec::kAttnHeadDimWide; }
 
 bool sizes_ok(int NL, int B, int H, int L_cap, int hd) {
@@ -93,8 +121,12 @@ struct SegArgs {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// clear_bytes > 0: the first clear_bytes of the workspace (its arrival counters) are
+// zeroed by a fill kernel on `stream` after every host check has passed, right before
+// the attention launch.
 int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int dtype,
-                float scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+                float scale, void* ws, size_t ws_bytes, hipStream_t stream,
+                size_t clear_bytes = 0) {
   for (int s = 0; s < nseg; ++s) {
     if (!segs[s].q || !segs[s].k || !segs[s].v || !segs[s].len || !segs[s].out) return DEC_E_NULL;
   }
@@ -193,6 +225,10 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   const int split = env_int("DECSTEP_ATTN_SPLIT", seqs < dec::kAttnSplitBelow ? 1 : 0);
   p.cpi = split ? 1 : (1 << 24);  // whole mode: every chunk of a sequence in one item
   if (nseg == 1) p.seg[1] = p.seg[0];
+  if (clear_bytes > 0 && lay.bytes > 0) {
+    const hipError_t ez = dec::fill_zero_launch(ws, clear_bytes, stream);
+    if (ez != hipSuccess) return hip_fail(ez);
+  }
   const hipError_t e = dec::attn_launch(p, dtype, env_int("DECSTEP_ATTN_BLOCKS", 0), stream);
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
@@ -260,6 +296,37 @@ int dec_attn_step_append(const void* q_self, void* k_self, void* v_self, const i
   s[0].v_new = v_new;
   return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, workspace, ws_bytes,
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+int dec_attn_step_noalloc(const void* q_self, const void* k_self, const void* v_self,
+                          const int32_t* len, int L_cap_self, float* out_self,
+                          const void* q_cross, const void* k_cross, const void* v_cross,
+                          const int32_t* enc_len, int L_cap_cross, float* out_cross,
+                          int n_layers, int B, int H, int hd, int dtype, float scale,
+                          dec_stream_t stream) {
+  // host checks first: nothing is looked up or enqueued for a call that fails them
+  if (!q_self || !k_self || !v_self || !len || !out_self || !q_cross || !k_cross || !v_cross ||
+      !enc_len || !out_cross)
+    return DEC_E_NULL;
+  if (dtype != DEC_BF16 && dtype != DEC_F32) return DEC_E_DTYPE;
+  if (!hd_ok(hd) || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 1 || L_cap_cross < 1)
+    return hd_ok(hd) ? DEC_E_SHAPE : DEC_E_UNSUPPORTED;
+  const int caps[2] = {L_cap_self, L_cap_cross};
+  if (!sizes_ok(n_layers, B, H, L_cap_self, hd) || !sizes_ok(n_layers, B, H, L_cap_cross, hd))
+    return DEC_E_SHAPE;
+  const WsLayout lay_max = ws_layout(n_layers, B, H, hd, caps, dec::kAttnChunk);
+  const WsLayout lay_min = ws_layout(n_layers, B, H, hd, caps, dec::kAttnMinChunk);
+  if (lay_max.bytes > kScratchBytes) return DEC_E_WORKSPACE;
+  const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
+                        {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
+  void* ws = nullptr;
+  if (lay_min.bytes > 0) {  // (lay_max needs a workspace only where lay_min does)
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  // both layouts start with the same two arrival-counter regions
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, ws, ws ? kScratchBytes : 0,
+                     reinterpret_cast<hipStream_t>(stream), 2 * lay_min.ticket_bytes);
 }
 
 int dec_attn_step_ex(const void* q_self, const void* k_self, const void* v_self,

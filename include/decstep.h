@@ -146,6 +146,31 @@ int dec_attn_step_append(const void* q_self, void* k_self, void* v_self, const i
                          int B, int H, int hd, int dtype, float scale, void* workspace,
                          size_t ws_bytes, dec_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under stream capture
+ * that may not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation): dec_attn_step without a workspace argument.  The arrival
+ * counters and chunk states live in a library-owned device array of
+ * DEC_NOALLOC_SCRATCH_BYTES bytes (one per GPU, held until the process
+ * ends); the call allocates and frees nothing.  The first call on a device
+ * takes the array's address there (a HIP symbol lookup, no allocation).
+ * Every call clears the array's arrival counters with a fill kernel on
+ * `stream` before the attention launch, so a call starts from zero whatever
+ * the previous one left.  The layout is the one a workspace of that size
+ * gets from dec_attn_step (the chunk states at 128 keys when they fit, else
+ * at 1024 keys), so outputs equal dec_attn_step's with such a workspace bit
+ * for bit.  A shape whose states fit neither way (dec_attn_workspace_bytes
+ * at 1024-key chunks above the array's size) returns DEC_E_WORKSPACE before
+ * anything is enqueued.  All calls on one GPU share the array: calls that
+ * overlap on a device (other streams, other threads) race and must be
+ * ordered by the caller.  Everything else as dec_attn_step. */
+#define DEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int dec_attn_step_noalloc(const void* q_self, const void* k_self, const void* v_self,
+                          const int32_t* len, int L_cap_self, float* out_self,
+                          const void* q_cross, const void* k_cross, const void* v_cross,
+                          const int32_t* enc_len, int L_cap_cross, float* out_cross,
+                          int n_layers, int B, int H, int hd, int dtype, float scale,
+                          dec_stream_t stream);
+
 /* dec_attn_step with two widenings (both optional):
  *   cross_mask  [B, mask_words] uint32, or NULL: an arbitrary boolean mask over
  *               the description ("A rough architecture of Parler TTS": the

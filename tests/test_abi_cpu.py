@@ -421,3 +421,19 @@ def test_order_key_map_is_monotone_over_all_float32_bit_patterns():
     kmin = np.zeros(1, np.uint32)
     dec.dec_order_keys_host(x, kmin, 1)
     assert kn[0] > kinf and kn[1] > kinf and kn[2] < kmin[0] and kn[3] < kmin[0]
+
+
+@_no_gpu
+def test_noalloc_step_host_validation():
+    def call(NL=24, B=1, H=16, hd=64, dt=0, caps=(4096, 1024), q=A, **kw):
+        return D.raw_status("dec_attn_step_noalloc", q, A, A, A, caps[0], A, A, A, A, A, caps[1],
+                            A, NL, B, H, hd, dt, ctypes.c_float(0.125), None)
+    assert call(q=None) == D.DEC_E_NULL
+    assert call(dt=5) == D.DEC_E_DTYPE
+    assert call(hd=96) == D.DEC_E_UNSUPPORTED
+    assert call(NL=0) == D.DEC_E_SHAPE
+    assert call(caps=(0, 1024)) == D.DEC_E_SHAPE
+    # chunk states beyond the library's fixed array: rejected before anything is enqueued
+    big = D.dec_attn_workspace_bytes(24, 64, 16, 64, 4096, 4096)
+    assert big > 16 << 20
+    assert call(B=64, caps=(4096, 4096)) == D.DEC_E_WORKSPACE
