@@ -29,7 +29,7 @@ def compile_flags(defines=()):
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              # floating point exactly as written: fused multiply-adds only where fmaf says so
              "-ffp-contract=off",
-             "-Wall", "-Wno-unused-function",
+             "-Wall", "-Wno-unused-function", "-Werror=uninitialized",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     flags += [f"-D{d}" for d in defines]
     return flags

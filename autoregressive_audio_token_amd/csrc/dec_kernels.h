@@ -117,6 +117,17 @@ struct AttnSeg {
   const void* v_new;
 };
 
+// One wave's first tile of a launch: the next launch requests the same bytes before it
+// has derived its own schedule, and keeps them when its first tile is that one.
+struct TileRec {
+  int tag;                // bit 0: valid; bit 1: segment 1
+  int row;                // (layer, b, head) row of the sequence
+  int key0;               // first key of the tile
+  int n;                  // valid keys of the sequence (rows of the load's buffer range)
+};
+constexpr int kAttnRecGroups = 4096;   // workgroups a workspace keeps first-tile records for
+constexpr int kAttnRecLdsPerWave = 8192;  // LDS bytes that hold one wave's requested tile
+
 struct AttnParams {
   AttnSeg seg[2];
   int nseg;
@@ -129,6 +140,10 @@ struct AttnParams {
   int chunk_log2;         // log2(keys per chunk); 0: the launcher chooses
   int min_chunk_log2;     // the smallest chunk the workspace holds partials for
   float qscale;           // scale * log2(e): scores are formed in base 2
+  int cus;                // compute units of the device (set by the launcher)
+  int balance;            // whole-sequence launches: cut the heavy excess in halves
+  TileRec* rec;           // [rec_groups][kAttnWaves] first tiles of the last launch, or null
+  int rec_groups;
 };
 
 // Upper bound on the work items of a launch (every sequence at full capacity).

@@ -82,6 +82,12 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 
+// After the layout: one first-tile record per wave of up to kAttnRecGroups workgroups
+// (the next launch requests those tiles while it derives its schedule).  Optional: a
+// workspace without room for it runs without.
+constexpr size_t kRecBytes = (size_t)dec::kAttnRecGroups * dec::kAttnWaves * sizeof(dec::TileRec);
+static_assert(kRecBytes % 256 == 0, "whole 256-byte blocks");
+
 bool hd_ok(int hd) { return hd == dec::kAttnHeadDim || hd == dec::kAttnHeadDimWide; }
 
 bool sizes_ok(int NL, int B, int H, int L_cap, int hd) {
@@ -92,11 +98,8 @@ bool sizes_ok(int NL, int B, int H, int L_cap, int hd) {
   return elems < (1LL << 46);
 }
 
-// Optional overrides for tuning and for the grid- and split-independence tests.
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return s == nullptr ? dflt : atoi(s);
-}
+// Launch-policy overrides of the calling thread (dec_tuning_set); all zero by default.
+thread_local dec_tuning g_tuning{};
 
 struct SegArgs {
   const void* q;
@@ -180,7 +183,7 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   const WsLayout& lay = small_ok ? lay_min : lay_max;
   const int min_log2 = dec::attn_log2(small_ok ? dec::kAttnMinChunk : dec::kAttnChunk);
   int chunk_log2 = 0;  // the launcher chooses
-  const int chunk_env = env_int("DECSTEP_ATTN_CHUNK", 0);
+  const int chunk_env = g_tuning.attn_chunk_keys;
   if (chunk_env != 0) {  // a fixed chunk (tests of every cut)
     if (!is_pow2(chunk_env) || chunk_env > dec::kAttnChunk || chunk_env < (1 << min_log2))
       return DEC_E_UNSUPPORTED;
@@ -188,6 +191,12 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   }
 
   dec::AttnParams p{};
+  if (ws != nullptr && aligned(ws, 16) && ws_bytes >= lay.bytes + kRecBytes) {
+    p.rec = reinterpret_cast<dec::TileRec*>(static_cast<char*>(ws) + lay.bytes);
+    p.rec_groups = dec::kAttnRecGroups;
+  }
+  p.balance = g_tuning.attn_no_halves ? 0 : 1;
+  if (g_tuning.attn_no_records) p.rec = nullptr;
   p.nseg = nseg;
   p.NL = NL;
   p.B = B;
@@ -222,14 +231,15 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   // Few sequences: every chunk is its own work item, so the CUs get equal bytes;
   // otherwise one workgroup owns a whole sequence (no cross-workgroup traffic).
   const long long seqs = (long long)NL * B * H * nseg;
-  const int split = env_int("DECSTEP_ATTN_SPLIT", seqs < dec::kAttnSplitBelow ? 1 : 0);
+  const int split = g_tuning.attn_schedule == 0 ? (seqs < dec::kAttnSplitBelow ? 1 : 0)
+                                                 : (g_tuning.attn_schedule == 1 ? 1 : 0);
   p.cpi = split ? 1 : (1 << 24);  // whole mode: every chunk of a sequence in one item
   if (nseg == 1) p.seg[1] = p.seg[0];
   if (clear_bytes > 0 && lay.bytes > 0) {
     const hipError_t ez = dec::fill_zero_launch(ws, clear_bytes, stream);
     if (ez != hipSuccess) return hip_fail(ez);
   }
-  const hipError_t e = dec::attn_launch(p, dtype, env_int("DECSTEP_ATTN_BLOCKS", 0), stream);
+  const hipError_t e = dec::attn_launch(p, dtype, g_tuning.attn_blocks, stream);
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
@@ -244,7 +254,7 @@ size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd, int L_cap_se
   if (!hd_ok(hd) || n_layers < 1 || B < 1 || H < 1 || L_cap_self < 0 || L_cap_cross < 0)
     return 0;
   const int caps[2] = {L_cap_self, L_cap_cross};
-  return ws_layout(n_layers, B, H, hd, caps, dec::kAttnMinChunk).bytes;
+  return ws_layout(n_layers, B, H, hd, caps, dec::kAttnMinChunk).bytes + kRecBytes;
 }
 
 int dec_attn_workspace_init(void* workspace, size_t ws_bytes, dec_stream_t stream) {
@@ -320,12 +330,10 @@ int dec_attn_step_noalloc(const void* q_self, const void* k_self, const void* v_
   const SegArgs s[2] = {{q_self, k_self, v_self, len, out_self, L_cap_self},
                         {q_cross, k_cross, v_cross, enc_len, out_cross, L_cap_cross}};
   void* ws = nullptr;
-  if (lay_min.bytes > 0) {  // (lay_max needs a workspace only where lay_min does)
-    const hipError_t e = scratch_address(&ws);
-    if (e != hipSuccess) return hip_fail(e);
-  }
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
   // both layouts start with the same two arrival-counter regions
-  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, ws, ws ? kScratchBytes : 0,
+  return attn_common(s, 2, n_layers, B, H, hd, dtype, scale, ws, kScratchBytes,
                      reinterpret_cast<hipStream_t>(stream), 2 * lay_min.ticket_bytes);
 }
 
@@ -578,9 +586,9 @@ int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n
   p.V_valid = V_valid;
   p.V_stride = V_stride;
   // the MFMA path stores 4 logits at a time and addresses h with 32-bit offsets
-  p.force_gemv = env_int("DECSTEP_HEAD_GEMV", 0) || !aligned(logits, 16) || V_stride % 4 != 0 ||
+  p.force_gemv = g_tuning.head_kernel == 1 || !aligned(logits, 16) || V_stride % 4 != 0 ||
                  (long long)(B + 32) * D * 2 > (1LL << 31) - 1;
-  p.mfma_cfg = env_int("DECSTEP_HEAD_CFG", 0);  // 0: the measured policy
+  p.mfma_cfg = g_tuning.head_mfma_cfg;  // 0: the measured policy
   const hipError_t e = dec::lm_head_launch(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
@@ -662,6 +670,28 @@ int dec_graph_destroy(void* exec) {
   if (exec == nullptr) return DEC_E_NULL;
   const hipError_t e = hipGraphExecDestroy(static_cast<hipGraphExec_t>(exec));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
+int dec_tuning_set(const dec_tuning* t) {
+  if (t == nullptr) {
+    g_tuning = dec_tuning{};
+    return DEC_OK;
+  }
+  const int ck = t->attn_chunk_keys;
+  if (ck != 0 && (!is_pow2(ck) || ck < 128 || ck > dec::kAttnChunk)) return DEC_E_SHAPE;
+  if (t->attn_schedule < 0 || t->attn_schedule > 2 || t->attn_blocks < 0 ||
+      t->attn_no_halves < 0 || t->attn_no_halves > 1 || t->attn_no_records < 0 ||
+      t->attn_no_records > 1 || t->head_kernel < 0 || t->head_kernel > 1 ||
+      t->head_mfma_cfg < 0 || t->head_mfma_cfg > 99)
+    return DEC_E_SHAPE;
+  g_tuning = *t;
+  return DEC_OK;
+}
+
+int dec_tuning_get(dec_tuning* t) {
+  if (t == nullptr) return DEC_E_NULL;
+  *t = g_tuning;
+  return DEC_OK;
 }
 
 int dec_last_hip_error(void) { return g_last_hip; }

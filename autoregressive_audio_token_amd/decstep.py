@@ -40,6 +40,13 @@ def _load():
 
 
 _lib = _load()
+
+
+class Tuning(ctypes.Structure):
+    """dec_tuning: launch-policy overrides of the calling thread (all 0: the defaults)."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "attn_chunk_keys", "attn_schedule", "attn_blocks", "attn_no_halves",
+        "attn_no_records", "head_kernel", "head_mfma_cfg")]
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
@@ -83,6 +90,8 @@ _SIGS = {
     "dec_graph_end": (_I, [_P, ctypes.POINTER(_P)]),
     "dec_graph_launch": (_I, [_P, _P]),
     "dec_graph_destroy": (_I, [_P]),
+    "dec_tuning_set": (_I, [ctypes.POINTER(Tuning)]),
+    "dec_tuning_get": (_I, [ctypes.POINTER(Tuning)]),
     "dec_last_hip_error": (_I, []),
     "dec_strerror": (ctypes.c_char_p, [_I]),
     "dec_order_keys_host": (None, [_P, _P, _SZ]),
@@ -312,6 +321,24 @@ def dec_graph_launch(exec_handle, stream=None):
 
 def dec_graph_destroy(exec_handle):
     _check(_lib.dec_graph_destroy(exec_handle))
+
+
+def dec_tuning_set(**fields):
+    """Set the calling thread's overrides (fields of Tuning; unnamed fields are 0).
+    No arguments restores the defaults."""
+    if not fields:
+        _check(_lib.dec_tuning_set(None))
+        return
+    unknown = set(fields) - {n for n, _ in Tuning._fields_}
+    if unknown:
+        raise TypeError(f"unknown tuning fields {sorted(unknown)}")
+    _check(_lib.dec_tuning_set(ctypes.byref(Tuning(**fields))))
+
+
+def dec_tuning_get():
+    t = Tuning()
+    _check(_lib.dec_tuning_get(ctypes.byref(t)))
+    return {n: getattr(t, n) for n, _ in Tuning._fields_}
 
 
 def dec_last_hip_error():

@@ -376,9 +376,9 @@ def heads_bench(a, w):
         return e0.elapsed_time(e1) * 1e3 / (3 * n_k)
 
     head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
-    os.environ["DECSTEP_HEAD_GEMV"] = "1"      # the vector-ALU kernel, for comparison
+    dec.dec_tuning_set(head_kernel=1)          # the vector-ALU kernel, for comparison
     gemv_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
-    del os.environ["DECSTEP_HEAD_GEMV"]
+    dec.dec_tuning_set()
     head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
     emb_us = timed(lambda i: dec.dec_embed_sum(toks, E, x, B, n_cb, S, D, stream))
     ok = bool(torch.isfinite(logits[:, :, :V]).all().item() and torch.isfinite(x).all().item())

@@ -62,10 +62,15 @@ enum dec_status {
  * whose chunks (counted at full capacity) would give fewer than one work item
  * per four CUs, halves the chunk (down to 128 keys) until they do, when its
  * workspace holds the chunk states at 128 keys (dec_attn_workspace_bytes
- * sizes it so).  The cut therefore depends
- * on n, the call's shape and capacities, the workspace size and the device's
- * CU count, never on the grid or on how chunks are spread over workgroups:
- * results are bitwise reproducible for a given call on a given device. */
+ * sizes it so).  A launch that gives each sequence one workgroup also cuts
+ * the excess of its heaviest sequences in halves: when the sequences of the
+ * longest length (each one chunk, of more than half a chunk) number a multiple
+ * of the CU count plus E, with E at least a quarter of the CU count, the last E
+ * of the longest group become two half-chunk items each, so the CUs carry
+ * nearly equal bytes.  The cut therefore depends on n, the call's shape and
+ * capacities, the workspace size and the device's CU count, never on the grid
+ * or on how chunks are spread over workgroups: results are bitwise
+ * reproducible for a given call on a given device. */
 int dec_attn_chunk_keys(void);
 
 /* Workspace bytes for attention over n_layers x B x H sequences with a self
@@ -79,7 +84,15 @@ int dec_attn_chunk_keys(void);
  * then keeps 1024-key chunks.  One workspace sized for both caches serves
  * dec_attn_self, dec_attn_cross and dec_attn_step of one n_layers x B x H
  * shape; calls of another shape need their own workspace, or
- * dec_attn_workspace_init in between.  Returns 0 on bad sizes. */
+ * dec_attn_workspace_init in between.  The size returned also holds, after the
+ * counters and states, 256 KiB of first-tile records: every wave of a launch
+ * records which tile it read first, and the next launch on the workspace
+ * requests that tile at once, before it has derived its own schedule, and
+ * keeps it only when its first tile is the same one (the address comes from the
+ * call's own arguments and is checked against them, so a record left by any
+ * other call costs at most bytes read in vain).  A workspace without room for
+ * the records runs without them; outputs are the same bit for bit.  Returns 0
+ * on bad sizes. */
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,
                                 int L_cap_self, int L_cap_cross);
 
@@ -120,8 +133,11 @@ int dec_attn_cross(const void* q, const void* k, const void* v, const int32_t* e
 
 /* Self-attention and cross-attention of the same step in ONE launch: equal to
  * dec_attn_self(q_self, ...) followed by dec_attn_cross(q_cross, ...), bit for
- * bit.  workspace must hold dec_attn_workspace_bytes(n_layers, B, H, hd,
- * L_cap_self, L_cap_cross) bytes. */
+ * bit, except where the halving above sees different heavy sequences in the
+ * joint launch than in the separate ones (both caches at the longest length);
+ * those outputs differ in rounding only, within the same bars.  workspace must
+ * hold dec_attn_workspace_bytes(n_layers, B, H, hd, L_cap_self, L_cap_cross)
+ * bytes. */
 int dec_attn_step(const void* q_self, const void* k_self, const void* v_self,
                   const int32_t* len, int L_cap_self, float* out_self,
                   const void* q_cross, const void* k_cross, const void* v_cross,
@@ -402,6 +418,37 @@ int dec_graph_launch(void* exec, dec_stream_t stream);
 int dec_graph_destroy(void* exec);
 
 /* The hipError_t of the last failed HIP call made by this thread. */
+/* Test and tuning overrides of the launch policy, for the calling thread only (the
+ * library keeps no other per-call state).  They change how work is cut and spread,
+ * never what is computed: every setting gives results within the same parity bars.
+ * The defaults (all fields 0) are what every product call uses; tests use the
+ * overrides to reach each schedule and to compare them bit for bit.
+ *   attn_chunk_keys  0: the launcher chooses; else keys per split-K chunk, a power of
+ *                    two from 128 to 1024 (a call whose workspace does not hold the
+ *                    chunk states at that chunk returns DEC_E_UNSUPPORTED)
+ *   attn_schedule    0: by call shape; 1: every chunk its own work item; 2: one
+ *                    workgroup per sequence (no cross-workgroup fold)
+ *   attn_blocks      0: the occupancy-sized persistent grid; else that many workgroups
+ *   attn_no_halves   1: whole-sequence launches never cut heavy sequences in halves
+ *   attn_no_records  1: launches do not request the tiles recorded by the last launch
+ *   head_kernel      0: by shape; 1: the vector-ALU kernel at every batch size
+ *   head_mfma_cfg    0: the measured policy; else 10 * row tiles + batch tiles per
+ *                    workgroup of the MFMA kernel
+ * dec_tuning_set(NULL) restores the defaults.  Returns DEC_E_SHAPE for a value out of
+ * range (nothing is changed). */
+typedef struct dec_tuning {
+  int attn_chunk_keys;
+  int attn_schedule;
+  int attn_blocks;
+  int attn_no_halves;
+  int attn_no_records;
+  int head_kernel;
+  int head_mfma_cfg;
+} dec_tuning;
+int dec_tuning_set(const dec_tuning* t);
+/* The calling thread's current overrides. */
+int dec_tuning_get(dec_tuning* t);
+
 int dec_last_hip_error(void);
 
 /* A static string naming a dec_status code. */

@@ -1,4 +1,6 @@
 """Calls into the HIP path through the C ABI, for the GPU tests."""
+import contextlib
+
 import numpy as np
 import torch
 
@@ -6,6 +8,20 @@ import autoregressive_audio_token_amd as dec
 
 DEV = "cuda:0"
 HD = 64
+
+
+@contextlib.contextmanager
+def tuning(**fields):
+    """Launch-policy overrides (dec_tuning) for the calls inside the block; the previous
+    overrides come back afterwards."""
+    before = dec.dec_tuning_get()
+    now = dict(before)
+    now.update(fields)
+    dec.dec_tuning_set(**now)
+    try:
+        yield
+    finally:
+        dec.dec_tuning_set(**before)
 
 
 def code(w):

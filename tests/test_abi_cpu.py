@@ -17,6 +17,8 @@ from autoregressive_audio_token_amd import decstep as D
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "decstep.h")
 A = 0x10000          # a fake, 16-byte aligned "device address" (never dereferenced)
+# the workspace's first-tile records: 4 waves x 16 bytes for each of up to 4096 workgroups
+REC = 4096 * 4 * 16
 
 # These cases hand fake addresses to the library; they are host-logic tests and run
 # only where no GPU is visible, so a case that slipped past validation could never
@@ -95,10 +97,11 @@ def test_attention_host_validation():
     assert _attn(q=A + 8) == D.DEC_E_ALIGN
     assert _attn(out=A + 2) == D.DEC_E_ALIGN
     # a cache longer than one chunk needs the workspace: at least the states at 1024-key
-    # chunks (two 256-byte ticket regions, 4 chunk states of 68 floats rounded to 1280 B)
+    # chunks (two 256-byte ticket regions, 4 chunk states of 68 floats rounded to 1280 B);
+    # the size asked for adds the states at 128-key chunks and the first-tile records
     L = 4 * dec.dec_attn_chunk_keys()
     need = dec.dec_attn_workspace_bytes(1, 1, 1, 64, L, 0)
-    assert need == 512 + 32 * 68 * 4
+    assert need == 512 + 32 * 68 * 4 + REC
     assert _attn(L=L, ws=None, wsb=0) == D.DEC_E_NULL
     assert _attn(L=L, ws=A, wsb=512 + 1280 - 1) == D.DEC_E_WORKSPACE
     assert _attn(L=L, ws=A + 4, wsb=need) == D.DEC_E_ALIGN
@@ -118,39 +121,39 @@ def test_step_validation_and_workspace_sizes():
     assert st == D.DEC_E_WORKSPACE
     ck = dec.dec_attn_chunk_keys()
     assert ck == 1024
-    # capacities within the smallest chunk (128 keys): no workspace at all
-    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 128, 128) == 0
+    # capacities within the smallest chunk (128 keys): no chunk states and no counters,
+    # only the optional first-tile records
+    assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 128, 128) == REC
     assert dec.dec_attn_workspace_bytes(24, 1, 16, 64, 129, 0) > 0
     # two ticket regions of 24 sequences (256 bytes each), then the chunk states at
     # 128-key chunks: 80 chunks of the self cache and 24 of the cross cache, 68 floats each
     s = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 0)
     c = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 0, 3 * ck)
     both = dec.dec_attn_workspace_bytes(2, 3, 4, 64, 10 * ck, 3 * ck)
-    assert s == 512 + 24 * 80 * 68 * 4 and c == 512 + 24 * 24 * 68 * 4
-    assert both == s + c - 512
+    assert s == 512 + 24 * 80 * 68 * 4 + REC and c == 512 + 24 * 24 * 68 * 4 + REC
+    assert both == s + c - 512 - REC
     assert dec.dec_attn_workspace_bytes(2, 3, 4, 32, 10, 10) == 0
     # head dim 128: chunk states of 4 + 128 floats
     w128 = dec.dec_attn_workspace_bytes(2, 3, 4, 128, 10 * ck, 0)
-    assert w128 == 512 + 24 * 80 * 132 * 4
+    assert w128 == 512 + 24 * 80 * 132 * 4 + REC
 
 
 
 @_no_gpu
-def test_workspace_down_to_the_1024_key_states(monkeypatch):
-    # An invalid fixed chunk is refused right after the workspace check, so these calls
-    # show which workspaces pass that check without launching anything.
+def test_workspace_down_to_the_1024_key_states(tune):
+    # A fixed 128-key chunk that the workspace holds no states for is refused right after
+    # the workspace check, so these calls show which workspaces pass that check without
+    # launching anything.
     def self_call(L_cap, ws, nbytes):
         return D.raw_status("dec_attn_self", A, A, A, A, A, 2, 3, 4, L_cap, 64, 0,
                             ctypes.c_float(0.125), ws, nbytes, None)
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "3")
+    with pytest.raises(D.DecError):
+        tune(attn_chunk_keys=3)                                   # not a power of two
+    tune(attn_chunk_keys=128)
     assert self_call(1024, None, 0) == D.DEC_E_UNSUPPORTED      # one 1024-key chunk: none
     small = 512 + 24 * 4 * 68 * 4                                 # 4 chunks at 1024 keys
     assert self_call(4096, A, small - 1) == D.DEC_E_WORKSPACE
     assert self_call(4096, A, small) == D.DEC_E_UNSUPPORTED
-    # a fixed chunk below what the workspace holds states for is refused
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "128")
-    assert self_call(4096, A, small) == D.DEC_E_UNSUPPORTED
-    assert self_call(1024, None, 0) == D.DEC_E_UNSUPPORTED
 
 
 def _samp(**kw):

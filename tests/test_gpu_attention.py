@@ -155,14 +155,14 @@ def test_fused_step_equals_separate_calls_and_runs_repeat_bitwise():
 
 @pytest.mark.parametrize("blocks", [1, 7, 256, 5000])
 @pytest.mark.parametrize("split", ["0", "1"])
-def test_grid_size_changes_no_bit(blocks, split, monkeypatch):
+def test_grid_size_changes_no_bit(blocks, split, tune):
     # both schedules: in split mode a small grid walks many chunk items per workgroup,
     # publishing each chunk state and folding a sequence when its last chunk arrives
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    tune(attn_schedule=1 if split == "1" else 2)
     w = configs.MINI_V1
     d = _inputs(w, self_lens=[1500], cross_lens=[64])
     ref_s, ref_c = [hp.host(t) for t in hp.attn_step(w, d)]
-    monkeypatch.setenv("DECSTEP_ATTN_BLOCKS", str(blocks))
+    tune(attn_blocks=int(blocks))
     o_s, o_c = [hp.host(t) for t in hp.attn_step(w, d)]
     assert np.array_equal(o_s, ref_s) and np.array_equal(o_c, ref_c)
 
@@ -189,15 +189,15 @@ def test_fp32_tiny_with_invalid_slots_poisoned_by_inf():
 
 @pytest.mark.parametrize("chunk", [128, 256, 512, 1024])
 @pytest.mark.parametrize("n", [700, 1024, 1025, 3000, 4096])
-def test_split_and_whole_sequence_modes_agree_bitwise(n, chunk, monkeypatch):
+def test_split_and_whole_sequence_modes_agree_bitwise(n, chunk, tune):
     # chunks spread over workgroups (folded by the last one to arrive) versus one
     # workgroup per sequence, at the same chunk: identical arithmetic, identical bits
     w = configs.MINI_V1
     d = _inputs(w, self_lens=[n])
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", str(chunk))
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "0")
+    tune(attn_chunk_keys=int(chunk), attn_no_halves=1)   # (halves cut a different chunk)
+    tune(attn_schedule=2)
     whole = hp.host(hp.attn("self", w, d))
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
+    tune(attn_schedule=1)
     split = hp.host(hp.attn("self", w, d))
     assert np.array_equal(whole, split)
     src = RowSource(w, [n], d["cross_len_host"])
@@ -206,7 +206,7 @@ def test_split_and_whole_sequence_modes_agree_bitwise(n, chunk, monkeypatch):
 
 
 @pytest.mark.parametrize("B,entry", [(40, "step"), (100, "self"), (1100, "self"), (2048, "step")])
-def test_many_groups_take_the_lds_work_list(B, entry, monkeypatch):
+def test_many_groups_take_the_lds_work_list(B, entry, tune):
     # More than 64 (segment, sequence) groups: the work list is built in LDS and binary
     # searched instead of in registers; above 1024 groups it stays in group order; 4096
     # groups (the step at B = 2048) is the most one launch takes.  Random lengths with
@@ -227,10 +227,10 @@ def test_many_groups_take_the_lds_work_list(B, entry, monkeypatch):
     ws = hp.workspace(w, w.self_cap, w.cross_cap)
     src = RowSource(w, s_len, c_len)
     rows = sampled_rows(w, B + 16, seed=B)
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "1024")
+    tune(attn_chunk_keys=1024)
     outs = {}
     for split in ("0", "1"):
-        monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+        tune(attn_schedule=1 if split == "1" else 2)
         if entry == "step":
             outs[split] = [hp.host(t) for t in hp.attn_step(w, d, ws)]
         else:
@@ -242,7 +242,7 @@ def test_many_groups_take_the_lds_work_list(B, entry, monkeypatch):
         _check("cross", w, d, torch.from_numpy(outs["0"][1]), src, rows, c_len)
 
 
-def test_per_layer_calls_equal_the_stacked_call_bitwise(monkeypatch):
+def test_per_layer_calls_equal_the_stacked_call_bitwise(tune):
     # the model-shaped schedule: one call per layer on offset pointers (a launch of
     # 16 sequences, which spreads chunks over workgroups) against one stacked launch.
     # At the stacked launch's 1024-key chunks the bits agree; left to choose, the
@@ -265,7 +265,7 @@ def test_per_layer_calls_equal_the_stacked_call_bitwise(monkeypatch):
                               w.scale, ws, nb)
         return hp.host(out)
     chosen = per_layer()
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "1024")
+    tune(attn_chunk_keys=1024)
     assert np.array_equal(per_layer(), stacked)
     src = RowSource(w, lens, d["cross_len_host"])
     rows = sampled_rows(w, 48, seed=2500)
@@ -275,15 +275,15 @@ def test_per_layer_calls_equal_the_stacked_call_bitwise(monkeypatch):
 @pytest.mark.parametrize("chunk", [128, 256])
 @pytest.mark.parametrize("n", [1, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1000, 2049,
                                4096])
-def test_small_chunks_ragged_lengths(n, chunk, monkeypatch):
+def test_small_chunks_ragged_lengths(n, chunk, tune):
     # a launch of few sequences (16 heads of one layer) cut into 128- or 256-key chunks,
     # each its own work item, folded by the last to arrive: every chunk edge
     import autoregressive_audio_token_amd as dec
     w = configs.MINI_V1
     lens = np.array([n], np.int32)
     d = _inputs(w, self_lens=lens)
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", str(chunk))
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
+    tune(attn_chunk_keys=int(chunk))
+    tune(attn_schedule=1)
     nb = dec.dec_attn_workspace_bytes(1, 1, w.heads, 64, w.self_cap, 0)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=hp.DEV)
     dec.dec_attn_workspace_init(ws, nb)
@@ -296,14 +296,14 @@ def test_small_chunks_ragged_lengths(n, chunk, monkeypatch):
     _check("self", w, d, out, src, rows, lens)
 
 
-def test_split_combine_is_stable_over_many_back_to_back_runs(monkeypatch):
+def test_split_combine_is_stable_over_many_back_to_back_runs(tune):
     # every 256-key chunk of every sequence is its own work item here (split mode forced:
     # left to choose, this 768-sequence launch keeps whole sequences); the last chunk of a
     # description to arrive folds the other three chunks' published states.  Many
     # unsynchronised launches must all produce the same bits, equal to the oracle within
     # the bar.
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", "1")
-    monkeypatch.setenv("DECSTEP_ATTN_CHUNK", "256")
+    tune(attn_schedule=1)
+    tune(attn_chunk_keys=256)
     w = configs.LONG_DESCRIPTION
     d = _inputs(w)
     ws = hp.workspace(w, w.self_cap, w.cross_cap)
@@ -344,3 +344,70 @@ def test_self_cross_and_step_calls_share_one_workspace():
     for kind, out, lens in (("self", o_self, s_len), ("self", s_step, s_len),
                             ("cross", c_step, c_len), ("cross", o_cross, c_len)):
         _check(kind, w, d, torch.from_numpy(out), src, rows, lens)
+
+
+def test_heavy_excess_cut_in_halves(tune):
+    # long_description: 384 description sequences of 1024 keys, each one whole item.  The
+    # excess over the CU count, E = 384 mod CUs (128 on a 256-CU part), is cut in halves
+    # (the last E sequences of the group); the rest stay whole.  Whole sequences keep
+    # their bits; halved ones fold two 512-key states instead of one 1024-key state and
+    # stay within the bars.
+    w = configs.LONG_DESCRIPTION
+    d = _inputs(w)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    E = (w.n_layers * w.heads) % cus
+    halves = hp.attn_step(w, d)
+    tune(attn_no_halves=1)
+    whole = hp.attn_step(w, d)
+    nlh = w.n_layers * w.heads
+    h_c, w_c = hp.host(halves[1]).reshape(nlh, -1), hp.host(whole[1]).reshape(nlh, -1)
+    assert np.array_equal(hp.host(halves[0]), hp.host(whole[0]))   # self: packed, never cut
+    if 4 * E >= cus:
+        assert np.array_equal(h_c[:nlh - E], w_c[:nlh - E])
+        assert not np.array_equal(h_c[nlh - E:], w_c[nlh - E:])
+    else:
+        assert np.array_equal(h_c, w_c)
+    src = RowSource(w, d["self_len_host"], d["cross_len_host"])
+    rows = all_rows(w)
+    _check("cross", w, d, halves[1], src, rows, d["cross_len_host"])
+
+
+def test_first_tile_records_change_no_bit(tune):
+    # Each wave records the tile it read first; the next launch on the same workspace
+    # requests that tile before deriving its schedule and keeps it only when its own first
+    # tile is the same.  Hits, misses, other lengths, other call shapes and records left by
+    # a larger call must all give the bits of launches that keep no records.
+    w = configs.MINI_V1
+    ws = hp.workspace(w, w.self_cap, w.cross_cap)
+    cases = [dict(self_lens=[1024]), dict(self_lens=[1024]), dict(self_lens=[700]),
+             dict(self_lens=[33]), dict(self_lens=[1024])]
+    for kw in cases:
+        d = _inputs(w, **kw)
+        with hp.tuning(attn_no_records=1):
+            ref = [hp.host(t) for t in hp.attn_step(w, d, ws)]
+        for _ in range(2):                       # the first may miss, the second hits
+            got = [hp.host(t) for t in hp.attn_step(w, d, ws)]
+            assert all(np.array_equal(a, b) for a, b in zip(got, ref)), kw
+        # a self-only call on the same workspace, then the step again
+        with hp.tuning(attn_no_records=1):
+            ref_s = hp.host(hp.attn("self", w, d, ws=ws))
+        assert np.array_equal(hp.host(hp.attn("self", w, d, ws=ws)), ref_s)
+        got = [hp.host(t) for t in hp.attn_step(w, d, ws)]
+        assert all(np.array_equal(a, b) for a, b in zip(got, ref))
+    # records of a 4-sequence batch, then a one-layer call whose rows are fewer: the
+    # recorded rows lie outside it and are not requested
+    import dataclasses
+    big = dataclasses.replace(w, batch=4)
+    small = dataclasses.replace(w, n_layers=1)
+    wsb = hp.workspace(big, w.self_cap, w.cross_cap)
+    db = _inputs(big)
+    hp.attn_step(big, db, wsb)
+    ds = _inputs(small)
+    with hp.tuning(attn_no_records=1):
+        ref = [hp.host(t) for t in hp.attn_step(small, ds, wsb)]
+    hp.attn_step(big, db, wsb)
+    got = [hp.host(t) for t in hp.attn_step(small, ds, wsb)]
+    assert all(np.array_equal(a, b) for a, b in zip(got, ref))
+    src = RowSource(small, ds["self_len_host"], ds["cross_len_host"])
+    _check("self", small, ds, torch.from_numpy(got[0]), src, all_rows(small),
+           ds["self_len_host"])

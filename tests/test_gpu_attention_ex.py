@@ -72,8 +72,8 @@ def _masked_case(seed, B=3):
 
 
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_cross_mask_matches_oracle(split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_cross_mask_matches_oracle(split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     w, d, enc, mask = _masked_case(4)
     mask[2, :] = False                  # no attended key: zeros
     mask[1, 299] = True                 # the last valid key
@@ -112,8 +112,8 @@ def test_all_true_mask_changes_no_bit():
 
 
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_fully_masked_tiles_are_not_read(split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_fully_masked_tiles_are_not_read(split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     w, d, enc, mask = _masked_case(6)
     mask[:, 64:192] = False             # whole tiles (32-key) of every sequence
     for name in ("k_cross", "v_cross"):  # NaN there: a read of them would show

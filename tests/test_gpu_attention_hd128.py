@@ -74,8 +74,8 @@ def test_parity_full(base):
 @pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1023, 1024,
                                1025, 2049, 4095, 4096])
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_ragged_lengths_both_schedules(n, split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_ragged_lengths_both_schedules(n, split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     w = _w(n_layers=4)
     lens = np.array([n], dtype=np.int32)
     d = _inputs(w, self_lens=lens)
@@ -84,7 +84,7 @@ def test_ragged_lengths_both_schedules(n, split, monkeypatch):
     _check("self", w, hp.attn("self", w, d), src, rows, lens)
 
 
-def test_schedules_are_bit_equal_and_batched_packing(monkeypatch):
+def test_schedules_are_bit_equal_and_batched_packing(tune):
     # 32 sequences of mixed lengths: short ones pack two to a workgroup
     w = _w(configs.BATCHED, n_layers=2)
     rng = np.random.default_rng(3)
@@ -94,7 +94,7 @@ def test_schedules_are_bit_equal_and_batched_packing(monkeypatch):
     ws = hp.workspace(w, w.self_cap, w.cross_cap)
     outs = []
     for split in ("1", "0"):
-        monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+        tune(attn_schedule=1 if split == "1" else 2)
         outs.append([hp.host(o) for o in hp.attn_step(w, d, ws=ws)])
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
@@ -131,8 +131,8 @@ def _paged(static, bs, extra_blocks, seed):
 
 
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_paged_equals_static(split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_paged_equals_static(split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     w = _w(n_layers=3, batch=4)
     lens = [2049, 33, 64, 0]
     d = _inputs(w, self_lens=lens)
@@ -169,8 +169,8 @@ def _pack(mask):
 
 
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_cross_mask_and_bf16_outputs(split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_cross_mask_and_bf16_outputs(split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     B = 3
     w = _w(n_layers=2, batch=B, cross_cap=512, cross_len=None, cross_len_range=(1, 512),
            self_len=100)

@@ -50,31 +50,31 @@ def _check_lm_head(B, D, seed):
 @pytest.mark.parametrize("B,D", [(1, 1024), (3, 1024), (17, 512), (32, 1024), (2, 2048),
                                  (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
 @pytest.mark.parametrize("path", ["default", "gemv"])
-def test_lm_head_matches_oracle(B, D, path, monkeypatch):
+def test_lm_head_matches_oracle(B, D, path, tune):
     # default: the MFMA kernel at every B; gemv: the vector-ALU kernel at every B
     if path == "gemv":
-        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
+        tune(head_kernel=1)
     print(f"[lm_head] B={B} D={D} path={path}", flush=True)
     _check_lm_head(B, D, 1000 + B * 7 + D)
 
 
 @pytest.mark.parametrize("B,D", [(3, 512), (20, 768), (40, 1024), (35, 1536), (19, 2048)])
 @pytest.mark.parametrize("cfg", [11, 12, 22, 42])
-def test_lm_head_every_mfma_tiling(B, D, cfg, monkeypatch):
+def test_lm_head_every_mfma_tiling(B, D, cfg, tune):
     # each row-tile x batch-tile choice of the MFMA kernel, at every model width: partial
     # batch tiles, several passes over the batch, the last row group partly past V_valid
-    monkeypatch.setenv("DECSTEP_HEAD_CFG", str(cfg))
+    tune(head_mfma_cfg=int(cfg))
     print(f"[lm_head mfma] B={B} D={D} cfg={cfg}", flush=True)
     _check_lm_head(B, D, 2000 + B * 7 + D + cfg)
 
 
 @pytest.mark.parametrize("B", [1, 9])
 @pytest.mark.parametrize("path", ["default", "gemv"])
-def test_lm_head_large_vocabulary(B, path, monkeypatch):
+def test_lm_head_large_vocabulary(B, path, tune):
     # a text-sized vocabulary (50,257 rows, odd, so the last row group is partial): many row
     # groups per codebook; padding columns untouched; the same relative bar
     if path == "gemv":
-        monkeypatch.setenv("DECSTEP_HEAD_GEMV", "1")
+        tune(head_kernel=1)
     n_cb, D, V = 2, 1024, 50257
     S = V + (-V) % 8
     print(f"[lm_head large V] B={B} V={V} path={path}", flush=True)

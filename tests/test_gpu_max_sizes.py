@@ -47,8 +47,8 @@ def _mean_pattern(n, hd):
 
 @pytest.mark.parametrize("dtype,hd", [("bf16", 64), ("f32", 128)])
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_largest_accepted_sequence(dtype, hd, split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_largest_accepted_sequence(dtype, hd, split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     tdt, code, eb = ((torch.bfloat16, dec.DEC_BF16, 2) if dtype == "bf16"
                      else (torch.float32, dec.DEC_F32, 4))
     cap = _largest_cap(hd, eb)

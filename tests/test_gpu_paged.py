@@ -55,8 +55,8 @@ def _static_out(w, d, lens_d, ws):
 
 @pytest.mark.parametrize("bs", [64, 256, 4096])
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_paged_self_equals_static_and_oracle(bs, split, monkeypatch):
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+def test_paged_self_equals_static_and_oracle(bs, split, tune):
+    tune(attn_schedule=1 if split == "1" else 2)
     w = _workload(len(LENS))
     print(f"[paged] bs={bs} split={split} lens={LENS}", flush=True)
     d = wdev.step_inputs(w, hp.DEV, self_lens=LENS)
@@ -140,10 +140,10 @@ def test_out_of_pool_table_entry_reads_zero_rows():
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("split", ["1", "0"])
-def test_paged_widened_step_equals_static_widened_step(out, split, monkeypatch):
+def test_paged_widened_step_equals_static_widened_step(out, split, tune):
     # a paged self cache with a masked description and fp32 / bf16 outputs in one launch
     # (dec_attn_step_paged_ex) against the static widened step on the same keys
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    tune(attn_schedule=1 if split == "1" else 2)
     w = dataclasses.replace(_workload(2), cross_cap=512, cross_len=None, cross_len_range=(1, 512))
     lens = [1500, 300]
     enc = np.array([512, 300], np.int32)

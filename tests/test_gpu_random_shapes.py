@@ -60,13 +60,13 @@ def _attention_case(seed):
 
 
 @pytest.mark.parametrize("seed", range(16))
-def test_attention_random_shapes(seed, monkeypatch):
+def test_attention_random_shapes(seed, tune):
     rng, w = _attention_case(seed)
     s_len, c_len = _lengths(rng, w.batch, w.self_cap), _lengths(rng, w.batch, w.cross_cap)
     entry = str(rng.choice(["self", "cross", "step", "ex"]))
     split = str(rng.choice(["auto", "0", "1"]))
     if split != "auto":
-        monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+        tune(attn_schedule=1 if split == "1" else 2)
     print(f"[random attn] seed={seed} NL={w.n_layers} B={w.batch} H={w.heads} hd={w.head_dim} "
           f"{w.dtype} caps=({w.self_cap},{w.cross_cap}) entry={entry} split={split}", flush=True)
     d = wdev.step_inputs(w, hp.DEV, self_lens=s_len, cross_lens=c_len)

@@ -221,13 +221,13 @@ def test_advancing_sampler_equals_sampler_at_each_step(k, uniforms):
 
 
 @pytest.mark.parametrize("split,chunk", [("0", None), ("1", None), ("1", "128"), ("1", "256")])
-def test_fused_append_equals_append_then_attention(split, chunk, monkeypatch):
+def test_fused_append_equals_append_then_attention(split, chunk, tune):
     # dec_attn_step_append against dec_kv_append + dec_attn_step on copies of the same
     # caches: outputs and both caches bit for bit.  Lengths at tile and chunk edges, the
     # full capacity, past it and non-positive (those append nothing).
-    monkeypatch.setenv("DECSTEP_ATTN_SPLIT", split)
+    tune(attn_schedule=1 if split == "1" else 2)
     if chunk:
-        monkeypatch.setenv("DECSTEP_ATTN_CHUNK", chunk)
+        tune(attn_chunk_keys=int(chunk))
     lens = np.array([1, 2, 32, 33, 64, 65, 129, 1024, 1025, 2048, 2049, 3000, 0, -3], np.int32)
     w = dataclasses.replace(configs.MINI_V1, n_layers=2, batch=len(lens), self_cap=2048,
                             self_len=None, self_len_range=(1, 2))
