@@ -110,6 +110,36 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int /*lane*/) {
   return v;
 }
 
+// The same scan over doubles: each DPP move carries both halves of a value.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ double dpp_f64_masked(double v) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)dpp_i32_masked<CTRL, ROW_MASK, BANK_MASK>((int)(uint32_t)bits);
+  const uint32_t hi =
+      (uint32_t)dpp_i32_masked<CTRL, ROW_MASK, BANK_MASK>((int)(uint32_t)(bits >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
+  const double x = v;
+  v += dpp_f64_masked<kDppRowShr1, 0xF, 0xF>(x);
+  v += dpp_f64_masked<kDppRowShr2, 0xF, 0xF>(x);
+  v += dpp_f64_masked<kDppRowShr3, 0xF, 0xF>(x);
+  v += dpp_f64_masked<kDppRowShr4, 0xF, 0xE>(v);
+  v += dpp_f64_masked<kDppRowShr8, 0xF, 0xC>(v);
+  v += dpp_f64_masked<kDppRowBcast15, 0xA, 0xF>(v);
+  v += dpp_f64_masked<kDppRowBcast31, 0xC, 0xF>(v);
+  return v;
+}
+
+// Lane `src`'s double, in every lane.
+__device__ __forceinline__ double readlane_f64(double v, int src) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bits, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bits >> 32), src);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int wave_exclusive_sum_int(int v, int lane) {
   return wave_inclusive_sum_int(v, lane) - v;
 }

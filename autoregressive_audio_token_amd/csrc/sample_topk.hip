@@ -237,13 +237,17 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
   const int need = kk - cnt_gt;  // entries equal to tau to keep, lowest index first
   const float m = key_value(kmax);
   const bool greedy = T <= 0.f;
-  // e = 2^((x - m) * log2(e) / T): one multiply by a per-row factor and the hardware
-  // exponential per entry, in place of a division and expf
-  // (held finite for a denormal T, so the row maximum still gets (x - m) * c2 = 0)
-  const float c2 = fminf(1.4426950408889634f / T, 3.4e38f);
-  float e[VPL], S[VPL];
+  // weights e = exp((x - m) / T) in float64, each rounded once to float32 and held; their
+  // sum Z in float64 (per lane in slot order, then across the wave); p = e / Z rounded
+  // once to float32 (the exported value).  The CDF the uniform is compared with is the
+  // float64 running sum of the exported probabilities in vocabulary order (one wave scan
+  // per slot plus the total of the slots before it).  Each p is within 3 x 2^-24 of the
+  // exact probability, so the CDF is within 3 x 2^-24 of the exact one.
+  const double md = (double)m, Td = (double)T;
+  double e[VPL];
   int pos[VPL];
   int eq_before = 0, kept_before = 0;
+  double zl = 0.0;  // this lane's share of Z
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const bool eq = idx[j] >= 0 && key[j] == tau;
@@ -251,38 +255,27 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
     const bool kept = key[j] > tau || (eq && eq_before + lanes_below(eqm) < need);
     const unsigned long long km = __ballot(kept);
     pos[j] = kept ? kept_before + lanes_below(km) : -1;
-    e[j] = kept && !greedy ? __builtin_amdgcn_exp2f((key_value(key[j]) - m) * c2) : 0.f;
+    e[j] = kept && !greedy ? exp(((double)key_value(key[j]) - md) / Td) : 0.0;
+    zl += e[j];
     eq_before += __popcll(eqm);
     kept_before += __popcll(km);
   }
-  // the slot scans are independent; only their totals chain: S[j] = run_j + scan_j with
-  // run_{j+1} = run_j + scan_j[63], the additions of a running sum in vocabulary order
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) S[j] = wave_inclusive_sum(e[j], lane);
-  float run = 0.f;  // sum of e over the slots before j
+  const double Zd = readlane_f64(wave_inclusive_sum_f64(zl), kWave - 1);
+  float pr[VPL];
+  int token = -1;  // the sampled index, before the delay mask
+  double run = 0.0;  // sum of the probabilities over the slots before j
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const float t = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S[j]), kWave - 1));
-    S[j] = run + S[j];
-    run = run + t;
+    pr[j] = (float)(e[j] / Zd);
+    const double C = run + wave_inclusive_sum_f64((double)pr[j]);
+    run = readlane_f64(C, kWave - 1);
+    // slots hold entries in vocabulary order (the whole row, or its compacted survivors):
+    // the first slot with a hit wins, and the token is that entry's index (greedy: the
+    // lowest index holding the largest key)
+    const unsigned long long hit = greedy ? __ballot(idx[j] >= 0 && key[j] == kmax)
+                                          : __ballot(pos[j] >= 0 && (double)u < C);
+    if (token < 0 && hit) token = __builtin_amdgcn_readlane(idx[j], __ffsll(hit) - 1);
   }
-  // run is now the inclusive sum at the last kept entry (later terms are zeros)
-  const float Z = run;
-  const float rZ = 1.f / Z;  // C = S * rZ and p = e * rZ: within 1.5 ulp of S / Z, e / Z
-  int token = -1;  // the sampled index, before the delay mask
-  unsigned long long hit[VPL];
-  if (greedy) {  // the lowest index holding the largest key
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) hit[j] = __ballot(idx[j] >= 0 && key[j] == kmax);
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) hit[j] = __ballot(pos[j] >= 0 && u < S[j] * rZ);
-  }
-  // slots hold entries in vocabulary order (the whole row, or its compacted survivors):
-  // the first slot with a hit wins, and the token is that entry's index
-#pragma unroll
-  for (int j = VPL - 1; j >= 0; --j)
-    if (hit[j]) token = __builtin_amdgcn_readlane(idx[j], __ffsll(hit[j]) - 1);
   if (token < 0) {  // rounding left u >= C_last: the last kept entry
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
@@ -297,7 +290,7 @@ __device__ __forceinline__ void sample_wide(const SampleParams& p, int row, cons
   for (int j = 0; j < VPL; ++j) {
     if (pos[j] < 0) continue;
     if (oi != nullptr) oi[pos[j]] = idx[j];
-    if (op != nullptr) op[pos[j]] = greedy ? (idx[j] == token ? 1.f : 0.f) : e[j] * rZ;
+    if (op != nullptr) op[pos[j]] = greedy ? (idx[j] == token ? 1.f : 0.f) : pr[j];
   }
   for (int t = kk + lane; t < p.top_k; t += kWave) {
     if (oi != nullptr) oi[t] = -1;
@@ -482,13 +475,16 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     sel = mk ? __ffsll(mk) - 1 : 0;
     prob = lane == sel ? 1.f : 0.f;
   } else {
-    const float e = act ? expf((xv - m) / T) : 0.f;
-    const float S = wave_inclusive_sum(e, lane);
-    const float Z = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, S), kk - 1));
-    const float C = S / Z;
-    const unsigned long long mk = __ballot(act && u < C);
+    // weights and their sum in fp64; each probability is rounded once to fp32 (the
+    // exported value), and the CDF the uniform is compared with is the fp64 running sum
+    // of those exported probabilities in vocabulary order, so it differs from the exact
+    // one by at most 2^-24 (the roundings of the probabilities) at any k
+    const double ed = act ? exp(((double)xv - (double)m) / (double)T) : 0.0;
+    const double Zd = readlane_f64(wave_inclusive_sum_f64(ed), kk - 1);
+    prob = act ? (float)(ed / Zd) : 0.f;
+    const double C = wave_inclusive_sum_f64((double)prob);
+    const unsigned long long mk = __ballot(act && (double)u < C);
     sel = mk ? __ffsll(mk) - 1 : kk - 1;
-    prob = e / Z;
   }
   int token = __builtin_amdgcn_readlane(xi, sel);
   if (!started) token = p.fill;

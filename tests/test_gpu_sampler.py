@@ -1,9 +1,10 @@
 """GPU parity of the fused sampler against the oracle, through the C ABI.
 
-Bars: top-k index sets bit-exact; tokens exact except rows whose uniform lies
-within 1e-6 of a CDF boundary of the oracle (either neighbour is then a correct
-token under rounding; such rows are counted and printed); probabilities within
-1e-6 absolute and their running sums within 1e-6 of the oracle's CDF.
+Bars (tests/sampler_check.py): top-k index sets bit-exact; each probability within
+half a float32 ulp of the oracle's; the CDF the kernel samples from (the float64
+running sum of the probabilities it exports) within 2^-24 of the oracle's and within
+5e-7; tokens exact except rows whose uniform lies within 1e-6 of an oracle CDF
+boundary, at most max(2, rows / 1000) such rows.
 """
 import numpy as np
 import pytest
@@ -13,9 +14,8 @@ pytestmark = pytest.mark.gpu
 
 from oracle import sampling as osamp  # noqa: E402
 from workloads import configs, gen, device as wdev  # noqa: E402
-from tests import hip_path as hp  # noqa: E402
+from tests import hip_path as hp, sampler_check  # noqa: E402
 
-BAND = 1e-6
 
 
 def _dev(a, dtype=None):
@@ -24,18 +24,9 @@ def _dev(a, dtype=None):
 
 def _compare(logits, V_valid, T, k, u, step, fill, tokens, idx, prob):
     want = osamp.sample(logits, V_valid, T, k, u, step, fill)
-    tokens, idx, prob = hp.host(tokens), hp.host(idx), hp.host(prob)
-    kk = min(k, V_valid)
-    assert np.array_equal(idx[..., :kk], want["topk_idx"][..., :kk]), "top-k sets differ"
-    assert np.all(idx[..., kk:] == -1) and np.all(prob[..., kk:] == 0)
-    near = want["dist"] < BAND
-    bad = (tokens != want["tokens"]) & ~near
-    assert not bad.any(), f"token mismatch at {np.argwhere(bad)[:5]}"
-    assert np.max(np.abs(prob[..., :kk] - want["topk_prob"][..., :kk])) <= BAND
-    cdf = np.cumsum(prob[..., :kk].astype(np.float64), axis=-1)
-    sampling_rows = np.asarray(T, np.float64)[:, None].repeat(logits.shape[1], 1) > 0
-    assert np.max(np.abs(cdf - want["cdf"][..., :kk])[sampling_rows]) <= BAND
-    print(f"  rows={tokens.size} boundary_excluded={int(near.sum())}", flush=True)
+    st = sampler_check.check(want, hp.host(tokens), hp.host(idx), hp.host(prob), T, k, V_valid)
+    print(f"  rows={st['rows']} boundary_excluded={st['excluded']} prob_err={st['prob_err']:.2e} "
+          f"cdf_err={st['cdf_err']:.2e}", flush=True)
     return want
 
 

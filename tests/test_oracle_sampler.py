@@ -163,3 +163,54 @@ def test_boundary_comparison_is_strict_and_overflow_takes_the_last():
     y = np.array([1.0, -4.0, 3.0, 2.0])
     assert S.sample_row(y, 1.0, 3, 1.0)[0] == 3
     assert S.sample_row(y, 1.0, 3, 7.5)[0] == 3
+
+
+# ---- dist: the distance from u to the nearest CDF boundary ------------------------------
+# It decides which token mismatches a GPU comparison may excuse (a uniform within the
+# band of a boundary makes either neighbour correct under rounding), so it is pinned on
+# hand-computed rows where every boundary is known exactly.
+
+def test_dist_two_equal_logits():
+    # x = [0, 0], T = 1, k = 2: p = [1/2, 1/2], boundaries C = [1/2, 1]
+    x = np.zeros(2)
+    for u, tok, dist in ((0.49, 0, 0.01), (0.5, 1, 0.0), (0.999, 1, 0.001), (0.0, 0, 0.5),
+                         (0.75, 1, 0.25)):
+        t, _, _, C, d = S.sample_row(x, 1.0, 2, u)
+        assert np.allclose(C, [0.5, 1.0], rtol=0, atol=1e-15)
+        assert t == tok and abs(d - dist) <= 1e-12, (u, t, d)
+
+
+def test_dist_four_boundaries():
+    # p proportional to 1, 2, 3, 4 (logits log 1 .. log 4): C = [0.1, 0.3, 0.6, 1.0]
+    x = np.log(np.array([1.0, 2.0, 3.0, 4.0]))
+    cases = ((0.05, 0, 0.05), (0.31, 2, 0.01), (0.29, 1, 0.01), (0.55, 2, 0.05),
+             (0.61, 3, 0.01), (0.8, 3, 0.2), (0.97, 3, 0.03))
+    for u, tok, dist in cases:
+        t, S_, p, C, d = S.sample_row(x, 1.0, 4, u)
+        assert np.allclose(p, [0.1, 0.2, 0.3, 0.4], rtol=0, atol=1e-15)
+        assert np.allclose(C, [0.1, 0.3, 0.6, 1.0], rtol=0, atol=1e-15)
+        assert t == tok and abs(d - dist) <= 1e-12, (u, t, d)
+
+
+def test_dist_counts_only_the_kept_set_and_its_order():
+    # vocabulary order [4, 1, 3, 2] scaled by log: kept (k = 3) = indices 0, 2, 3 with
+    # weights 4, 3, 2 in ascending index order: C = [4/9, 7/9, 1]; index 1 is dropped
+    x = np.log(np.array([4.0, 1.0, 3.0, 2.0]))
+    t, kept, p, C, d = S.sample_row(x, 1.0, 3, 0.5)
+    assert list(kept) == [0, 2, 3]
+    assert np.allclose(C, [4 / 9, 7 / 9, 1.0], rtol=0, atol=1e-15)
+    assert t == 2 and abs(d - (0.5 - 4 / 9)) <= 1e-12
+    # temperature 2 flattens the weights to sqrt: 2, sqrt 3, sqrt 2
+    w = np.sqrt([4.0, 3.0, 2.0])
+    t, kept, p, C, d = S.sample_row(x, 2.0, 3, 0.5)
+    Cw = np.cumsum(w) / w.sum()
+    assert np.allclose(C, Cw, rtol=0, atol=1e-15)
+    assert abs(d - np.min(np.abs(0.5 - Cw))) <= 1e-12
+
+
+def test_dist_single_kept_entry_and_greedy():
+    x = np.array([5.0, 0.0, 0.0, 0.0])
+    t, _, _, C, d = S.sample_row(x, 1.0, 1, 0.3)
+    assert t == 0 and list(C) == [1.0] and abs(d - 0.7) <= 1e-12
+    t, _, _, _, d = S.sample_row(x, 0.0, 4, 0.3)
+    assert t == 0 and d == np.inf                   # greedy rows have no boundary
