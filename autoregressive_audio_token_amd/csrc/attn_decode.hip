@@ -36,7 +36,6 @@
 //     each).  The work list is derived on the device from len[] (device
 //     resident, so a captured graph stays valid as lengths change), longest
 //     sequences first; a persistent, occupancy-sized grid walks it.
-#include <atomic>
 
 #include "dec_common.h"
 #include "dec_kernels.h"
@@ -820,13 +819,18 @@ long long attn_items_cap(const AttnParams& p) {
 }
 
 namespace {
-// Per-device launch facts, filled on first use.  Threads may launch concurrently, so the
-// fields are relaxed atomics: every writer stores the same value.
-struct DevInfo {
-  std::atomic<int> cus{0};
-  std::atomic<int> occ[2][2][5] = {};  // resident workgroups per CU [dtype][head dim 64/128][variant]
+// Per-device launch facts, filled on a thread's first launch on the device: each thread
+// keeps its own copy, so no state is shared between threads.  0 = not yet queried.
+struct Occupancy {
+  size_t lds;  // the dynamic LDS bytes it was queried for
+  int wgs;     // resident workgroups per CU
 };
-DevInfo g_dev[64];
+struct DevInfo {
+  int cus = 0;
+  Occupancy occ[2][2][5] = {};  // [dtype][head dim 64/128][variant]
+};
+constexpr int kDevInfoSlots = 64;
+thread_local DevInfo t_dev[kDevInfoSlots];
 
 // variant: 0 static, 1 paged, 2 widened (key masks / bf16 outputs, static caches), 3 static
 // with the current token's rows appended, 4 widened with a paged self cache
@@ -890,12 +894,12 @@ hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_
   {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    DevInfo& di = g_dev[dev & 63];
-    cus = di.cus.load(std::memory_order_relaxed);
+    const bool cached = dev >= 0 && dev < kDevInfoSlots;
+    cus = cached ? t_dev[dev].cus : 0;
     if (cus == 0) {
       e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess) return e;
-      di.cus.store(cus, std::memory_order_relaxed);
+      if (cached) t_dev[dev].cus = cus;
     }
   }
   if (choose_chunk) {
@@ -919,13 +923,14 @@ hipError_t attn_launch(const AttnParams& p_in, int dtype, int blocks, hipStream_
   if (p.cpi == 1 || p.min_chunk_log2 >= p.chunk_log2 || G > kWave) p.balance = 0;
   if (blocks <= 0) {
     hipError_t e = hipSuccess;
-    DevInfo& di = g_dev[dev & 63];
-    int occ = di.occ[dtype][wide][variant].load(std::memory_order_relaxed);
-    if (occ == 0 || G > 64) {
+    Occupancy* slot = dev >= 0 && dev < kDevInfoSlots ? &t_dev[dev].occ[dtype][wide][variant]
+                                                      : nullptr;
+    int occ = slot != nullptr && slot->lds == lds ? slot->wgs : 0;
+    if (occ == 0) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kAttnThreads, lds);
       if (e != hipSuccess) return e;
       if (occ < 1) occ = 1;
-      if (G <= 64) di.occ[dtype][wide][variant].store(occ, std::memory_order_relaxed);
+      if (slot != nullptr) *slot = Occupancy{lds, occ};
     }
     const long long cap = attn_items_cap(p);
     const long long want = (long long)cus * occ;

@@ -4,9 +4,11 @@
 A step is one pass of the whole hot path over one batch: self-attention over
 the valid prefix of the static cache and cross-attention over the description
 for all layers (one fused launch), then the fused top-k sampler over the 9
-codebooks.  Steps run as a captured hipGraph that chains one step per cache
-set; the R cache sets are distinct allocations so each step reads cold data
-(R x valid bytes exceeds the 256 MB Infinity Cache).
+codebooks.  Exactly --warmup untimed and --steps timed steps run, each on the
+next of R cache sets in rotation; the sets are distinct allocations, so each
+step reads cold data (R x valid bytes exceeds the 256 MB Infinity Cache).  The
+timed steps run as min(10, steps) captured hipGraphs of near-equal size, with
+HIP events between them (per-block step times beside the total).
 
 Prints ONE JSON line: value = valid K/V bytes per step / time per step (GB/s).
 
@@ -78,7 +80,10 @@ def parse(argv=None):
     ap.add_argument("--calibrate", action="store_true",
                     help="the calibration kernels: streaming reads at 4 MiB, the workload's\n"
                          "valid bytes and 4 GiB, and the cost of an empty graph node")
-    return ap.parse_args(argv)
+    a = ap.parse_args(argv)
+    if a.steps < 1 or a.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return a
 
 
 def read_probe(dec, torch, nbytes, dev, stream, launches, min_pool=1 << 30):
@@ -661,44 +666,59 @@ def main(argv=None):
                           "outputs_finite": bool(torch.isfinite(o_s).all().item())}),
               flush=True)
         return 0
+    # Exactly `warmup` untimed steps, then exactly `steps` timed ones, each step on the next
+    # cache set in rotation (no set is read twice within R steps, so a step finds its K/V
+    # bytes in HBM, not in a cache).  The timed steps run as min(10, steps) captured graphs
+    # of near-equal size with an event between graphs: the per-block step times come from
+    # those events, `value` from the first and last.  The warm-up runs in graphs of the
+    # same size.  Graphs are keyed by (first set, steps), so equal blocks share one.
+    graphs = {}
+
+    def block_graph(first, n):
+        key = (first % R, n)
+        if key not in graphs:
+            with torch.cuda.stream(stream):
+                dec.dec_graph_begin(stream)
+                for j in range(n):
+                    attn(sets[(first + j) % R], stream)
+                    sample(stream)
+                graphs[key] = dec.dec_graph_end(stream)
+        return graphs[key]
+
+    def split(total, parts):
+        q, r = divmod(total, parts)
+        return [q + 1] * r + [q] * (parts - r)
+
+    steps = a.steps
+    n_blocks = min(10, steps)
+    timed = split(steps, n_blocks)
+    warm = split(a.warmup, -(-a.warmup // max(timed))) if a.warmup > 0 else []
+    plan, pos = [], 0
+    for n in warm + timed:
+        plan.append(block_graph(pos, n))
+        pos += n
     with torch.cuda.stream(stream):
         dec.dec_attn_workspace_init(ws, nb, stream)
-        for st in sets:                  # eager warm-up of every set
-            attn(st, stream)
-            sample(stream)
-        stream.synchronize()
-        dec.dec_graph_begin(stream)
-        for st in sets:
-            attn(st, stream)
-            sample(stream)
-        graph = dec.dec_graph_end(stream)
-
-    log(f"{R} cache sets captured; timing")
-    launches = max(1, math.ceil(a.steps / R))
-    steps = launches * R
-    warm = max(1, math.ceil(a.warmup / R))
-    for _ in range(warm):
-        dec.dec_graph_launch(graph, stream)
+    log(f"{R} cache sets, {len(graphs)} graphs captured; {a.warmup} warm-up and {steps} timed "
+        f"steps in {len(warm)} + {n_blocks} graphs")
+    for g in plan[:len(warm)]:
+        dec.dec_graph_launch(g, stream)
     stream.synchronize()
     torch.cuda.synchronize()
-    # one continuous timed region of `launches` graph replays; events at up to ten block
-    # boundaries inside it give per-block step times (their median is reported beside the
-    # total, which is what `value` is computed from)
-    n_blocks = min(10, launches)
-    bounds = [round(i * launches / n_blocks) for i in range(n_blocks + 1)]
     evs_blk = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
     t0 = time.perf_counter()
     evs_blk[0].record(stream)
-    for i in range(n_blocks):
-        for _ in range(bounds[i + 1] - bounds[i]):
-            dec.dec_graph_launch(graph, stream)
+    for i, g in enumerate(plan[len(warm):]):
+        dec.dec_graph_launch(g, stream)
         evs_blk[i + 1].record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = evs_blk[0].elapsed_time(evs_blk[-1]) / steps
-    blk_us = sorted(evs_blk[i].elapsed_time(evs_blk[i + 1]) * 1e3 / ((bounds[i + 1] - bounds[i]) * R)
+    blk_us = sorted(evs_blk[i].elapsed_time(evs_blk[i + 1]) * 1e3 / timed[i]
                     for i in range(n_blocks))
+    for g in graphs.values():
+        dec.dec_graph_destroy(g)
     out_ok = bool(torch.isfinite(o_s).all().item() and torch.isfinite(o_c).all().item())
     tok_h = tok.cpu().numpy()
     tok_ok = bool(np.all((tok_h >= 0) & (tok_h < w.vocab_valid) | (tok_h == w.fill_token)))
@@ -735,7 +755,6 @@ def main(argv=None):
     per = sorted(s0.elapsed_time(s1) * 1e3 for s0, s1 in evs)        # microseconds
     pair_us = sum(per) / len(per)
     achieved = valid / (k_us * 1e-6) / 1e9
-    dec.dec_graph_destroy(graph)
     # the measured ceiling: a plain streaming read of the same byte count in one launch
     probe_us, probe_gbs, probe_sets = read_probe(dec, torch, valid, dev, stream, n_k)
     # the sampler alone: a captured graph of n_k launches
@@ -771,10 +790,11 @@ def main(argv=None):
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm * R,
+        "warmup": a.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
-        "us_per_step_blocks": {"blocks": n_blocks, "median": round(blk_us[len(blk_us) // 2], 3),
+        "us_per_step_blocks": {"blocks": n_blocks, "steps_per_block": [min(timed), max(timed)],
+                               "median": round(blk_us[len(blk_us) // 2], 3),
                                "min": round(blk_us[0], 3), "max": round(blk_us[-1], 3)},
         "higher_is_better": True,
         "scaling": "weak",
@@ -791,10 +811,10 @@ def main(argv=None):
             "static_cache_bytes_per_set": static_bytes,
             "kv_layout": (f"self cache paged, {a.paged} keys per block" if a.paged
                           else "static caches"),
-            "schedule": (f"model-shaped: hipGraph of R steps; step = {attn_entry} "
+            "schedule": (f"model-shaped: one hipGraph per timed block; step = {attn_entry} "
                          f"({attn_launches} launches) + {samp_entry}" if model else
-                         f"hipGraph of R steps; step = {attn_entry} (self+cross, all layers, "
-                         f"one launch) + {samp_entry}"),
+                         f"one hipGraph per timed block; step = {attn_entry} (self+cross, "
+                         f"all layers, one launch) + {samp_entry}"),
             "variant": {"head_dim": w.head_dim, "cross_mask": mask_note,
                         "attention_outputs": "bf16" if a.out_bf16 else "f32",
                         "logits": "bf16" if a.logits_bf16 else "f32", "top_k": top_k},

@@ -315,8 +315,11 @@ int dec_sample_topk_philox(const float* logits, int B, int n_cb, int V_valid, in
  *                 its uniform from Philox4x64-10 with `seed` exactly as
  *                 dec_sample_topk_philox does
  * Rule, outputs, delay mask and device-side behaviour as dec_sample_topk.  For
- * top_k <= 64 the kernel is dec_sample_topk's; above it the CDF is accumulated
- * in float32 over the kept entries in vocabulary order, 64 at a time. */
+ * top_k <= 64 the kernel is dec_sample_topk's; above it the same arithmetic runs
+ * over the kept entries 64 at a time in vocabulary order.  Both form the weights
+ * exp((x - max) / T) and their sum in float64, round each probability once to
+ * float32 (what topk_prob holds), and compare u with the float64 running sum of
+ * those probabilities. */
 int dec_sample_topk_ex(const void* logits, int logits_dtype, int B, int n_cb, int V_valid,
                        int V_stride, const float* temperature, int top_k, const float* uniforms,
                        uint64_t seed, const int32_t* step, int32_t fill_token, int32_t* tokens,
@@ -417,7 +420,6 @@ int dec_graph_end(dec_stream_t stream, void** exec);
 int dec_graph_launch(void* exec, dec_stream_t stream);
 int dec_graph_destroy(void* exec);
 
-/* The hipError_t of the last failed HIP call made by this thread. */
 /* Test and tuning overrides of the launch policy, for the calling thread only (the
  * library keeps no other per-call state).  They change how work is cut and spread,
  * never what is computed: every setting gives results within the same parity bars.
@@ -449,6 +451,7 @@ int dec_tuning_set(const dec_tuning* t);
 /* The calling thread's current overrides. */
 int dec_tuning_get(dec_tuning* t);
 
+/* The hipError_t of the last failed HIP call made by this thread. */
 int dec_last_hip_error(void);
 
 /* A static string naming a dec_status code. */

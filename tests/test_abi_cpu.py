@@ -440,3 +440,120 @@ def test_noalloc_step_host_validation():
     big = D.dec_attn_workspace_bytes(24, 64, 16, 64, 4096, 4096)
     assert big > 16 << 20
     assert call(B=64, caps=(4096, 4096)) == D.DEC_E_WORKSPACE
+
+
+# ---- the Python binding's checks -------------------------------------------------------
+
+def _prototypes():
+    """{name: [(param name, is_pointer)]} from the header's function declarations."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(dec_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        if params.strip() in ("", "void"):
+            out[name] = []
+            continue
+        out[name] = [(re.findall(r"\w+", p)[-1], "*" in p or "dec_stream_t" in p)
+                     for p in params.split(",")]
+    return out
+
+
+def test_binding_declarations_follow_the_header():
+    """Every entry point the binding declares has the header's parameters: the same
+    names in the same order, pointers where the header has pointers."""
+    protos = _prototypes()
+    for name, params in D._DECL.items():
+        want = protos[name]
+        got = [(p.name, p.dims is not None or p.kind == "stream") for p in params]
+        # the executable graph handle is a pointer the binding takes as an integer
+        want = [("exec_handle", True) if n == "exec" else (n, ptr) for n, ptr in want]
+        got = [(n, True) if n == "exec_handle" else (n, ptr) for n, ptr in got]
+        assert got == want, name
+
+
+_SIZES = dict(n_layers=2, B=3, H=2, L_cap=5, hd=64, L_cap_self=7, L_cap_cross=6, n_cb=4,
+              V_valid=40, V_stride=48, top_k=3, mask_words=2, n_blocks=3, block_size=64,
+              max_blocks=2, D=16, V_emb=9, bytes=64, ws_bytes=256)
+
+
+def _good_call(params):
+    """CPU tensors and integers that satisfy every declaration of one entry point."""
+    import torch
+    dt = {"x": torch.bfloat16, "o": torch.float32, "l": torch.bfloat16, "bf16": torch.bfloat16,
+          "f32": torch.float32, "i32": torch.int32, "u32": torch.int32, "bytes": torch.uint8}
+    ints = {n: v for n, v in _SIZES.items()}
+    ints.update(dtype=D.DEC_BF16, out_dtype=D.DEC_F32, logits_dtype=D.DEC_BF16)
+    args = {}
+    for p in params:
+        if p.dims is not None:
+            shape = [d if isinstance(d, int) else ints[d] for d in p.dims]
+            args[p.name] = torch.zeros(shape, dtype=dt[p.kind])
+        elif p.kind == "stream":
+            args[p.name] = None
+        elif p.kind == "float":
+            args[p.name] = 0.125
+        else:
+            args[p.name] = ints.get(p.name, 0)
+    return args
+
+
+def test_binding_rejects_bad_tensors_before_the_call():
+    """For every buffer of every entry point: a wrong element type, a transposed
+    (non-contiguous) view, a wrong element count, a host tensor and a numpy array are
+    each refused by the binding (DecError with its status), never passed on.  Host
+    tensors of the right kind are refused as not on a GPU, so nothing reaches the
+    library here."""
+    import torch
+    for name, params in D._DECL.items():
+        fn = getattr(dec, name)
+        good = _good_call(params)
+        buffers = [p for p in params if p.dims is not None]
+        if not buffers:
+            continue
+        with pytest.raises(dec.DecError) as e:
+            fn(**good)
+        assert e.value.status == D.DEC_E_UNSUPPORTED and "not on a GPU" in str(e.value), name
+        for p in buffers:
+            t = good[p.name]
+            bad = {}
+            if p.kind != "bytes":
+                other = torch.float64 if t.dtype != torch.float64 else torch.float32
+                bad["dtype"] = (t.to(other), D.DEC_E_DTYPE)
+                bad["count"] = (torch.cat([t.reshape(-1), t.reshape(-1)[:1]]), D.DEC_E_SHAPE)
+            else:
+                bad["count"] = (t[:-1], D.DEC_E_SHAPE)
+            flat = t.reshape(-1)
+            if flat.numel() > 1:
+                wide = torch.zeros(flat.numel() * 2, dtype=t.dtype)
+                bad["layout"] = (wide[::2], D.DEC_E_SHAPE)
+                if t.dim() >= 2 and t.shape[-1] > 1 and t.shape[-2] > 1:
+                    bad["transposed"] = (t.transpose(-1, -2), D.DEC_E_SHAPE)
+            bad["numpy"] = (np.zeros(t.numel(), np.float32), D.DEC_E_UNSUPPORTED)
+            for what, (value, status) in bad.items():
+                args = dict(good)
+                args[p.name] = value
+                with pytest.raises(dec.DecError) as e:
+                    fn(**args)
+                assert e.value.status == status, (name, p.name, what, str(e.value))
+                assert p.name in str(e.value), (name, p.name, what, str(e.value))
+
+
+@_no_gpu
+def test_binding_passes_raw_addresses_and_none_unchecked():
+    """Integers are device addresses and None is NULL: the binding leaves them to the
+    library, whose own check answers (here DEC_E_NULL for a required NULL)."""
+    with pytest.raises(dec.DecError) as e:
+        dec.dec_step_advance(None, None, 3, None)
+    assert e.value.status == D.DEC_E_NULL
+    with pytest.raises(dec.DecError) as e:
+        dec.dec_probe_read(None, 16, A, None)
+    assert e.value.status == D.DEC_E_NULL
+
+
+def test_host_key_map_checks_its_arrays():
+    x = np.zeros(4, np.float32)
+    with pytest.raises(dec.DecError):
+        dec.dec_order_keys_host(x, np.zeros(4, np.int32), 4)
+    with pytest.raises(dec.DecError):
+        dec.dec_order_keys_host(x, np.zeros(3, np.uint32), 4)
+    with pytest.raises(dec.DecError):
+        dec.dec_order_keys_host(x.astype(np.float64), np.zeros(4, np.uint32), 4)

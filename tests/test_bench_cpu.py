@@ -4,6 +4,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -84,3 +86,11 @@ def test_oracle_baseline_reports_the_median_of_at_least_ten_steps():
     assert abs(r["value"] - valid / (r["us_per_step"] * 1e-6) / 1e9) <= 1e-3 * r["value"] + 1e-4
     assert r["host_cores_visible"] >= 1 and r["host_cpu_count"] >= r["host_cores_visible"]
     assert isinstance(r["host_cpu"], str) and r["host_cpu"]
+
+
+def test_steps_and_warmup_are_validated():
+    for argv in (["--steps", "0"], ["--warmup", "-1"]):
+        with pytest.raises(SystemExit):
+            bench.parse(argv)
+    a = bench.parse(["--steps", "20", "--warmup", "5"])
+    assert (a.steps, a.warmup) == (20, 5)

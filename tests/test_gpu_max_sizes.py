@@ -72,7 +72,13 @@ def test_largest_accepted_sequence(dtype, hd, split, tune):
     err = np.max(np.abs(got - want)) / np.max(np.abs(want))
     print(f"  max_rel_err={err:.3e}", flush=True)
     assert err <= BAR
-    # one key more is refused on the host, before any launch
+    # one key more is refused on the host, before any launch: by the binding (the tensors
+    # hold one key fewer than that shape), and by the library itself, reached with raw
+    # addresses, which the binding passes on unchecked
     with pytest.raises(dec.DecError) as e:
         dec.dec_attn_self(q, k, v, lens, out, 1, 1, 1, cap + 1, hd, code, hd ** -0.5, ws, nb)
+    assert e.value.status == dec.DEC_E_SHAPE
+    with pytest.raises(dec.DecError) as e:
+        dec.dec_attn_self(q, k.data_ptr(), v.data_ptr(), lens, out, 1, 1, 1, cap + 1, hd, code,
+                          hd ** -0.5, ws, nb)
     assert e.value.status == dec.DEC_E_UNSUPPORTED
