@@ -599,9 +599,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
     if (REC && rec_pending) {
       const int key0 = (c0 << iclog) + wave_part * KPT;
       const bool has = wave_ok && key0 < n;
+      // an appending launch takes key n - 1 of a self sequence from the new rows, never
+      // from the cache, so a record one key shorter (the last step's) holds every row
+      // this launch reads from memory (records exist only with the list in registers, so
+      // lane b holds sequence b's length as given)
+      const bool grown = APP && !cross && S.k_new != nullptr && n == spec.n + 1 &&
+                         __builtin_amdgcn_readlane(len_raw, b) <= S.L_cap;
       spec_hit = spec_live && has && spec.tag == (1 | (cross ? 2 : 0)) &&
                  spec.row == (int)wave_sidx && spec.key0 == key0 &&
-                 (spec.n == n || key0 + KPT <= min(n, spec.n));
+                 (spec.n == n || key0 + KPT <= min(n, spec.n) || grown);
       if (lane == 0)
         p.rec[blockIdx.x * kAttnWaves + wave] =
             has ? TileRec{1 | (cross ? 2 : 0), (int)wave_sidx, key0, n} : TileRec{0, 0, 0, 0};

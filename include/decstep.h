@@ -90,7 +90,9 @@ int dec_attn_chunk_keys(void);
  * requests that tile at once, before it has derived its own schedule, and
  * keeps it only when its first tile is the same one (the address comes from the
  * call's own arguments and is checked against them, so a record left by any
- * other call costs at most bytes read in vain).  A workspace without room for
+ * other call costs at most bytes read in vain).  In dec_attn_step_append a record
+ * one key shorter also serves: that key is the current token's, taken from the
+ * new rows.  A workspace without room for
  * the records runs without them; outputs are the same bit for bit.  Returns 0
  * on bad sizes. */
 size_t dec_attn_workspace_bytes(int n_layers, int B, int H, int hd,

@@ -252,3 +252,38 @@ def test_fused_append_equals_append_then_attention(split, chunk, tune):
     assert np.array_equal(_bits(o_c), _bits(ref_c))
     assert np.array_equal(_bits(d["k_self"]), _bits(k2))
     assert np.array_equal(_bits(d["v_self"]), _bits(v2))
+
+
+def test_appending_records_over_growing_lengths(tune):
+    # A decode loop's self lengths grow by one per step, so a short sequence's first tile
+    # straddles its length every step; the appending kernel takes key len - 1 from the new
+    # rows, so a record one key shorter still serves.  Steps with and without records on
+    # copies of the same caches: outputs and caches bit for bit at every step, including a
+    # jump past the capacity (nothing appended: the record one key shorter must not serve)
+    # and a return below it.
+    w = dataclasses.replace(configs.MINI_V1, n_layers=2, batch=3, self_cap=96,
+                            self_len=None, self_len_range=(1, 2))
+    steps = np.array([[1, 31, 93], [2, 32, 94], [3, 33, 95], [4, 34, 98], [5, 35, 99],
+                      [6, 36, 96], [7, 37, 97]], np.int32)
+    print(f"[append records] lens per step {steps.tolist()}", flush=True)
+    d = wdev.step_inputs(w, hp.DEV, self_lens=steps[0],
+                         fill_lens=(np.full(w.batch, w.self_cap), d_cross_lens(w)))
+    runs = []
+    for records in (True, False):
+        ws, nb = hp.workspace(w, w.self_cap, w.cross_cap)
+        runs.append(dict(records=records, ws=ws, nb=nb, k=d["k_self"].clone(),
+                         v=d["v_self"].clone(), len=d["len"].clone()))
+    for s, lens in enumerate(steps):
+        kn, vn = _dev(gen.new_rows(w, "k", s)), _dev(gen.new_rows(w, "v", s))
+        outs = []
+        for r in runs:
+            r["len"].copy_(torch.from_numpy(lens))
+            o_s, o_c = hp.out_buf(w), hp.out_buf(w)
+            with hp.tuning(attn_no_records=0 if r["records"] else 1):
+                dec.dec_attn_step_append(d["q_self"], r["k"], r["v"], r["len"], w.self_cap, o_s,
+                                         kn, vn, d["q_cross"], d["k_cross"], d["v_cross"],
+                                         d["enc_len"], w.cross_cap, o_c, w.n_layers, w.batch,
+                                         w.heads, 64, dec.DEC_BF16, w.scale, r["ws"], r["nb"])
+            outs.append([_bits(o_s), _bits(o_c), _bits(r["k"]), _bits(r["v"])])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b), (s, lens.tolist())
