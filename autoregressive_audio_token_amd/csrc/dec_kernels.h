@@ -180,7 +180,6 @@ hipError_t sample_launch(const SampleParams& p, hipStream_t stream);
 // ---- merged LM head and embedding sum ----------------------------------------------------
 
 constexpr int kHeadWaves = 4;   // 8-row groups (one per wave) per workgroup
-constexpr int kHeadBT = 16;     // rows of h staged in LDS at a time
 
 struct HeadParams {
   const uint16_t* h;      // [B, D] bf16

@@ -585,9 +585,13 @@ int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n
   p.n_cb = n_cb;
   p.V_valid = V_valid;
   p.V_stride = V_stride;
-  // the MFMA path stores 4 logits at a time and addresses h with 32-bit offsets
-  p.force_gemv = g_tuning.head_kernel == 1 || !aligned(logits, 16) || V_stride % 4 != 0 ||
-                 (long long)(B + 32) * D * 2 > (1LL << 31) - 1;
+  // B <= 2 is a matrix-vector product: the vector ALU (measured faster at B = 1 and equal
+  // at B = 2); larger batches on MFMA, which stores 4 logits at a time and addresses h
+  // with 32-bit offsets
+  const bool mfma_ok = aligned(logits, 16) && V_stride % 4 == 0 &&
+                       (long long)(B + 32) * D * 2 <= (1LL << 31) - 1;
+  const int kernel = g_tuning.head_kernel;  // 0: by shape, 1: vector ALU, 2: MFMA if it can
+  p.force_gemv = !mfma_ok || kernel == 1 || (kernel == 0 && B <= 2);
   p.mfma_cfg = g_tuning.head_mfma_cfg;  // 0: the measured policy
   const hipError_t e = dec::lm_head_launch(p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DEC_OK : hip_fail(e);
@@ -681,7 +685,7 @@ int dec_tuning_set(const dec_tuning* t) {
   if (ck != 0 && (!is_pow2(ck) || ck < 128 || ck > dec::kAttnChunk)) return DEC_E_SHAPE;
   if (t->attn_schedule < 0 || t->attn_schedule > 2 || t->attn_blocks < 0 ||
       t->attn_no_halves < 0 || t->attn_no_halves > 1 || t->attn_no_records < 0 ||
-      t->attn_no_records > 1 || t->head_kernel < 0 || t->head_kernel > 1 ||
+      t->attn_no_records > 1 || t->head_kernel < 0 || t->head_kernel > 2 ||
       t->head_mfma_cfg < 0 || t->head_mfma_cfg > 99)
     return DEC_E_SHAPE;
   g_tuning = *t;

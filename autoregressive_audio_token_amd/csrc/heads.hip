@@ -7,16 +7,14 @@
 // Parler TTS": the decoder takes the nine tokens of a step at once, so its
 // input is the sum of the nine codebooks' embedding rows.
 //
-// LM head: logits[b, c, v] = <h[b], W[c, v]> for v < V_valid.  At decode batch
-// sizes this is a matrix-vector product bound by reading W once (~20 MB at
-// 9 x 1089 x 1024 bf16), so it runs on the vector ALU with v_dot2c_f32_bf16, not
-// MFMA.  A wave owns 8 consecutive rows of one codebook, one row per group of 8
-// lanes; a lane reads 16 bytes of each 128-byte segment of its row, so every
-// load instruction covers whole cache lines, and all of the wave's loads are in
-// flight before h is needed.  A buffer descriptor spans the codebook's V_valid
-// rows, so the padding rows of a partial last group are never read.  h is
-// staged in LDS in batch tiles of kHeadBT rows and read back per segment; the
-// 8 lanes of a row reduce with DPP.
+// LM head: logits[b, c, v] = <h[b], W[c, v]> for v < V_valid.  At decode batch sizes
+// the product is bound by reading W once (~20 MB at 9 x 1089 x 1024 bf16).  At B <= 2 it
+// is a matrix-vector product and runs on the vector ALU (lm_head_kernel,
+// v_dot2c_f32_bf16); larger batches run on MFMA (lm_head_mfma_kernel), where each load of
+// h serves many rows of W.  Both read W in whole 128-byte lines in the same order: a
+// workgroup owns 16 rows of one codebook, its 4 waves split D into quarters, and 8
+// consecutive lanes read one line.  A buffer descriptor spans the codebook's V_valid
+// rows, so the padding rows of a partial last group are never read.
 #include "dec_common.h"
 #include "dec_kernels.h"
 
@@ -44,45 +42,55 @@ constexpr int kBufNonTemporal = 2;
 
 }  // namespace
 
+// Small batches: the product on the vector ALU (v_dot2c_f32_bf16), with W read exactly as
+// the MFMA kernel below reads it.  A workgroup owns 16 rows of one codebook and its 4
+// waves split D into quarters; load t gives lane l row (l >> 3) + 8 (t & 1), columns
+// (t >> 1) * 64 + (l & 7) * 8 .. + 8 of the wave's quarter, so 8 consecutive lanes read
+// one whole 128-byte line.  Per batch row, a lane dots its slices with the same columns
+// of h (read straight from memory: 16 bytes per 64 columns), the 8 lanes of a row add
+// with DPP, and the four quarter sums meet in LDS in wave order.  Rows of W at or past
+// V_valid read as zero through the descriptor and are not stored.
 template <int NSEG>
 __global__ __launch_bounds__(kHeadWaves * kWave) void lm_head_kernel(HeadParams p) {
   constexpr int D = NSEG * 64;
-  __shared__ u32x4 s_h[kHeadBT * D / 8];  // kHeadBT rows of h, bf16
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
-  const int grp = lane >> 3;  // row within the wave's 8
-  const int sl = lane & 7;    // 16-byte slice of each 128-byte segment
-  const int rgpc = (p.V_valid + 7) >> 3;  // 8-row groups per codebook
-  const int rg = blockIdx.x * kHeadWaves + wave;
-  const bool active = rg < p.n_cb * rgpc;  // uniform per wave
-  const int c = active ? rg / rgpc : 0;
-  const int v = (active ? rg - c * rgpc : 0) * 8 + grp;
+  constexpr int Q = D / kHeadWaves;        // columns per wave
+  constexpr int LT = 2 * Q / 64;           // loads per wave: two row halves per 64 columns
+  __shared__ float s_q[2][kHeadWaves][16];  // quarter sums, double-buffered over b
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
+  const int rgpc = (p.V_valid + 15) / 16;  // 16-row groups per codebook
+  const int c = blockIdx.x / rgpc;
+  const int v0 = (blockIdx.x - c * rgpc) * 16;
+  const int col = wave * Q + (lane & 7) * 8;  // this lane's first column
 
-  // W rows of codebook c: rows at or past V_valid lie outside the descriptor
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.W + (size_t)c * p.V_stride * D), 0,
-      active ? p.V_valid * D * 2 : 0, kBufWord3);
-  u32x4 w[NSEG];
-  const int row_off = v * D * 2 + sl * 16;
+      const_cast<uint16_t*>(p.W + (size_t)c * p.V_stride * D), 0, p.V_valid * D * 2, kBufWord3);
+  u32x4 w[LT];
 #pragma unroll
-  for (int s = 0; s < NSEG; ++s)
-    w[s] = __builtin_amdgcn_raw_buffer_load_b128(rw, row_off + s * 128, 0, kBufNonTemporal);
-
-  for (int b0 = 0; b0 < p.B; b0 += kHeadBT) {
-    const int bt = min(kHeadBT, p.B - b0);
-    __syncthreads();  // the previous tile of h has been read
-    const u32x4* hs = reinterpret_cast<const u32x4*>(p.h + (size_t)b0 * D);
-    for (int i = tid; i < bt * D / 8; i += kHeadWaves * kWave) s_h[i] = hs[i];
-    __syncthreads();
-    if (!active) continue;
-    for (int bb = 0; bb < bt; ++bb) {
-      float acc = 0.f;
+  for (int t = 0; t < LT; ++t)
+    w[t] = __builtin_amdgcn_raw_buffer_load_b128(
+        rw, ((v0 + (lane >> 3) + 8 * (t & 1)) * D + col + (t >> 1) * 64) * 2, 0, kBufNonTemporal);
+  for (int b = 0; b < p.B; ++b) {
+    const u32x4* hb = reinterpret_cast<const u32x4*>(p.h + (size_t)b * D + col);
+    float acc0 = 0.f, acc1 = 0.f;  // rows (l >> 3) and (l >> 3) + 8
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s) acc = dot8(w[s], s_h[bb * (D / 8) + s * 8 + sl], acc);
-      acc = group_sum<8>(acc);
-      if (sl == 0 && v < p.V_valid)
-        p.logits[((size_t)(b0 + bb) * p.n_cb + c) * p.V_stride + v] = acc;
+    for (int j = 0; j < LT / 2; ++j) {
+      const u32x4 hv = hb[j * 8];  // columns j * 64 + (l & 7) * 8 .. + 8 of the quarter
+      acc0 = dot8(w[2 * j], hv, acc0);
+      acc1 = dot8(w[2 * j + 1], hv, acc1);
+    }
+    acc0 = group_sum<8>(acc0);
+    acc1 = group_sum<8>(acc1);
+    float* const q = s_q[b & 1][wave];
+    if ((lane & 7) == 0) {
+      q[lane >> 3] = acc0;
+      q[(lane >> 3) + 8] = acc1;
+    }
+    __syncthreads();  // (double buffering: the other half is rewritten only after the next)
+    if (wave == 0 && lane < 16 && v0 + lane < p.V_valid) {
+      const float (*qs)[16] = s_q[b & 1];
+      p.logits[((size_t)b * p.n_cb + c) * p.V_stride + v0 + lane] =
+          ((qs[0][lane] + qs[1][lane]) + qs[2][lane]) + qs[3][lane];
     }
   }
 }
@@ -239,8 +247,7 @@ static hipError_t lm_head_launch_n(const HeadParams& p, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  const int groups = p.n_cb * ((p.V_valid + 7) / 8);
-  const int blocks = (groups + kHeadWaves - 1) / kHeadWaves;
+  const int blocks = p.n_cb * ((p.V_valid + 15) / 16);
   hipLaunchKernelGGL(lm_head_kernel<NSEG>, dim3(blocks), dim3(kHeadWaves * kWave), 0, stream, p);
   return hipGetLastError();
 }

@@ -381,10 +381,14 @@ def heads_bench(a, w):
         return e0.elapsed_time(e1) * 1e3 / (3 * n_k)
 
     head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
-    dec.dec_tuning_set(head_kernel=1)          # the vector-ALU kernel, for comparison
-    gemv_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
+    kernel_us = {}
+    for name, code in (("vector_alu", 1), ("mfma", 2)):   # each kernel alone, for comparison
+        dec.dec_tuning_set(head_kernel=code)
+        kernel_us[name] = timed(
+            lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
     dec.dec_tuning_set()
     head_us = timed(lambda i: dec.dec_lm_head(h, Ws[i % R], logits, B, D, n_cb, V, S, stream))
+    path = "vector_alu" if B <= 2 else "mfma"   # the library's choice at this batch size
     emb_us = timed(lambda i: dec.dec_embed_sum(toks, E, x, B, n_cb, S, D, stream))
     ok = bool(torch.isfinite(logits[:, :, :V]).all().item() and torch.isfinite(x).all().item())
     achieved = alg / (head_us * 1e-6) / 1e9
@@ -400,7 +404,8 @@ def heads_bench(a, w):
                    "vocab": V, "vocab_stride": S, "weight_sets": R,
                    "algorithmic_bytes_per_launch": alg},
         "roofline": {"bound": "hbm",
-                     "kernel": "lm_head_mfma_kernel (dec_lm_head)",
+                     "kernel": ("lm_head_kernel" if path == "vector_alu" else
+                                "lm_head_mfma_kernel") + " (dec_lm_head)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "measured_read_gbs": round(probe_gbs, 1),
@@ -411,8 +416,9 @@ def heads_bench(a, w):
                      "avg_launch_us": round(head_us, 3),
                      "avg_launch_us_method": f"HIP events around a captured graph of {n_k} "
                                              f"launches, 3 replays"},
-        "lm_head_path": "mfma",
-        "vector_alu_kernel_us": round(gemv_us, 3),
+        "lm_head_path": path,
+        "vector_alu_kernel_us": round(kernel_us["vector_alu"], 3),
+        "mfma_kernel_us": round(kernel_us["mfma"], 3),
         "embed_sum_us": round(emb_us, 3),
         "checks": {"outputs_finite": ok},
     }

@@ -374,10 +374,12 @@ int dec_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
  *           v >= V_valid are left untouched
  * No bias.  fp32 accumulation.  D one of 512, 768, 1024, 1536, 2048, else
  * DEC_E_UNSUPPORTED; (V_valid + 64) * D * 2 below 2^31 bytes; h and W 16-byte
- * aligned, logits 4-byte aligned.  Device pointers, caller-owned.  The product
- * runs on MFMA when logits is 16-byte aligned, V_stride a multiple of 4 and
- * (B + 32) * D * 2 below 2^31 bytes (otherwise on the vector ALU); both round
- * differently but stay within the same fp32 accumulation bound. */
+ * aligned, logits 4-byte aligned.  Device pointers, caller-owned.  At B <= 2 the
+ * product is a matrix-vector product and runs on the vector ALU; larger batches run
+ * on MFMA when logits is 16-byte aligned, V_stride a multiple of 4 and
+ * (B + 32) * D * 2 below 2^31 bytes (otherwise on the vector ALU too).  Both kernels
+ * read W in whole cache lines in the same order; they round differently but stay
+ * within the same fp32 accumulation bound. */
 int dec_lm_head(const void* h, const void* W, float* logits, int B, int D, int n_cb,
                 int V_valid, int V_stride, dec_stream_t stream);
 
@@ -435,7 +437,8 @@ int dec_graph_destroy(void* exec);
  *   attn_blocks      0: the occupancy-sized persistent grid; else that many workgroups
  *   attn_no_halves   1: whole-sequence launches never cut heavy sequences in halves
  *   attn_no_records  1: launches do not request the tiles recorded by the last launch
- *   head_kernel      0: by shape; 1: the vector-ALU kernel at every batch size
+ *   head_kernel      0: by shape; 1: the vector-ALU kernel at every batch size; 2: the
+ *                    MFMA kernel wherever its alignment allows
  *   head_mfma_cfg    0: the measured policy; else 10 * row tiles + batch tiles per
  *                    workgroup of the MFMA kernel
  * dec_tuning_set(NULL) restores the defaults.  Returns DEC_E_SHAPE for a value out of

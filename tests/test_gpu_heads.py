@@ -49,11 +49,12 @@ def _check_lm_head(B, D, seed):
 
 @pytest.mark.parametrize("B,D", [(1, 1024), (3, 1024), (17, 512), (32, 1024), (2, 2048),
                                  (5, 768), (1, 1536), (16, 1024), (33, 1024), (64, 1536)])
-@pytest.mark.parametrize("path", ["default", "gemv"])
+@pytest.mark.parametrize("path", ["default", "gemv", "mfma"])
 def test_lm_head_matches_oracle(B, D, path, tune):
-    # default: the MFMA kernel at every B; gemv: the vector-ALU kernel at every B
-    if path == "gemv":
-        tune(head_kernel=1)
+    # default: the vector-ALU kernel at B <= 2, MFMA above; gemv / mfma: that kernel at
+    # every B
+    if path != "default":
+        tune(head_kernel=1 if path == "gemv" else 2)
     print(f"[lm_head] B={B} D={D} path={path}", flush=True)
     _check_lm_head(B, D, 1000 + B * 7 + D)
 
@@ -69,12 +70,11 @@ def test_lm_head_every_mfma_tiling(B, D, cfg, tune):
 
 
 @pytest.mark.parametrize("B", [1, 9])
-@pytest.mark.parametrize("path", ["default", "gemv"])
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
 def test_lm_head_large_vocabulary(B, path, tune):
-    # a text-sized vocabulary (50,257 rows, odd, so the last row group is partial): many row
-    # groups per codebook; padding columns untouched; the same relative bar
-    if path == "gemv":
-        tune(head_kernel=1)
+    # 50,257 rows (odd, so the last row group is partial): many row groups per codebook;
+    # padding columns untouched; the same relative bar
+    tune(head_kernel=1 if path == "gemv" else 2)
     n_cb, D, V = 2, 1024, 50257
     S = V + (-V) % 8
     print(f"[lm_head large V] B={B} V={V} path={path}", flush=True)
