@@ -511,6 +511,94 @@ def cpu_baseline(w, seconds):
             "host_cpu_count": os.cpu_count()}
 
 
+def cpu_baseline_all_cores(w, seconds):
+    """The oracle, as it stands, on every host core: worker processes, forked before this
+    process makes any GPU call, each own a share of a step's (segment, layer, sequence)
+    attention tasks (the last also runs the sampler) and build their own inputs.  A step
+    starts every worker at a barrier and ends when the last one is done; BLAS runs one
+    thread per worker.  Returns None if a worker fails."""
+    import multiprocessing as mp
+    import threading
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attn as oattn, sampling as osamp
+    from workloads import configs, gen
+
+    s_len, c_len = gen.lengths(w)
+    lens = {"self": s_len, "cross": c_len}
+    tasks = [(kind, layer, b) for kind in ("self", "cross") for layer in range(w.n_layers)
+             for b in range(w.batch)]
+    n_workers = max(1, min(len(os.sched_getaffinity(0)), len(tasks)))
+    ctx = mp.get_context("fork")
+    ready, start, done = (ctx.Barrier(n_workers + 1) for _ in range(3))
+    stop = ctx.Value("i", 0)
+    limit = 300.0  # seconds any barrier may wait: a dead worker breaks the barriers
+
+    def work(i):
+        try:
+            share = tasks[i::n_workers]
+            q = {k: gen.queries(w, k) for k in ("self", "cross")}
+            rows = {t: (gen.kv_rows(w, t[0], "k", t[1], t[2], int(lens[t[0]][t[2]])),
+                        gen.kv_rows(w, t[0], "v", t[1], t[2], int(lens[t[0]][t[2]])))
+                    for t in share}
+            sampler = i == n_workers - 1
+            if sampler:
+                lg, u, T = gen.logits(w), gen.uniforms(w), gen.temperatures(w)
+            dec16 = (oattn.bf16_bits_to_f64 if w.dtype == "bf16"
+                     else (lambda x: x.astype(np.float64)))
+            with threadpool_limits(1):
+                ready.wait(limit)
+                while True:
+                    start.wait(limit)
+                    if stop.value:
+                        break
+                    for kind, layer, b in share:
+                        K, V = rows[kind, layer, b]
+                        for h in range(w.heads):
+                            oattn.attend_one(dec16(q[kind][layer, b, h]), dec16(K[h]),
+                                             dec16(V[h]), int(lens[kind][b]), w.scale)
+                    if sampler:
+                        osamp.sample(lg, w.vocab_valid, T, w.top_k, u, None, w.fill_token)
+                    done.wait(limit)
+        except Exception:
+            for bar in (ready, start, done):
+                bar.abort()
+        os._exit(0)  # no interpreter teardown in a forked child
+
+    procs = [ctx.Process(target=work, args=(i,), daemon=True) for i in range(n_workers)]
+    for p in procs:
+        p.start()
+    times = []
+    try:
+        ready.wait(limit)
+        t0 = time.perf_counter()
+        while len(times) < 10 or time.perf_counter() - t0 < seconds:
+            s = time.perf_counter()
+            start.wait(limit)
+            done.wait(limit)
+            times.append(time.perf_counter() - s)
+        stop.value = 1
+        start.wait(limit)
+    except threading.BrokenBarrierError:
+        times = []
+    for p in procs:
+        p.join(30)
+        if p.is_alive():
+            p.kill()
+    if not times:
+        return None
+    valid = configs.valid_kv_bytes(w, s_len, c_len)
+    med = statistics.median(times)
+    return {"value": round(valid / med / 1e9, 4), "unit": "GB/s", "cores": n_workers,
+            "kind": "oracle",
+            "sample": f"{len(times)} whole decode steps of {w.name}, float64 NumPy, the step's "
+                      f"{len(tasks)} (segment, layer, sequence) tasks shared by {n_workers} "
+                      f"worker processes (one thread each; the last also samples); value from "
+                      f"the median step time",
+            "us_per_step": round(med * 1e6, 1),
+            "us_per_step_mean": round(sum(times) / len(times) * 1e6, 1)}
+
+
 def main(argv=None):
     a = parse(argv)
     if a.gpus != 1:
@@ -543,6 +631,10 @@ def main(argv=None):
         print("--schedule model goes with the static caches and fp32 outputs", file=sys.stderr)
         return 2
     plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k or model)
+    all_cores = None
+    if not a.no_cpu_baseline:  # its worker processes are forked before any GPU call
+        log("timing the oracle on all host cores")
+        all_cores = cpu_baseline_all_cores(w, a.cpu_seconds)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s_len, c_len = gen.lengths(w)
@@ -862,6 +954,7 @@ def main(argv=None):
     if not a.no_cpu_baseline:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+        result["cpu_baseline"]["all_cores"] = all_cores
     print(json.dumps(result), flush=True)
     return 0 if (out_ok and tok_ok) else 1
 

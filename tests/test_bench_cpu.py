@@ -94,3 +94,16 @@ def test_steps_and_warmup_are_validated():
             bench.parse(argv)
     a = bench.parse(["--steps", "20", "--warmup", "5"])
     assert (a.steps, a.warmup) == (20, 5)
+
+
+def test_oracle_baseline_on_all_cores_runs_whole_steps_in_worker_processes():
+    from workloads import configs, gen
+    r = bench.cpu_baseline_all_cores(configs.TINY, 0.0)
+    assert r is not None, "a worker failed"
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert 1 <= r["cores"] <= len(os.sched_getaffinity(0))
+    steps = int(r["sample"].split()[0])
+    assert steps >= 10
+    s_len, c_len = gen.lengths(configs.TINY)
+    valid = configs.valid_kv_bytes(configs.TINY, s_len, c_len)
+    assert abs(r["value"] - valid / (r["us_per_step"] * 1e-6) / 1e9) <= 1e-3 * r["value"] + 1e-4
