@@ -638,6 +638,14 @@ int dec_probe_empty(dec_stream_t stream) {
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
+int dec_probe_clock(uint64_t* clocks, dec_stream_t stream) {
+  static_assert(dec::kProbeClockSlots == DEC_PROBE_CLOCK_SLOTS, "header and kernel agree");
+  if (clocks == nullptr) return DEC_E_NULL;
+  if (!aligned(clocks, 8)) return DEC_E_ALIGN;
+  const hipError_t e = dec::probe_clock_launch(clocks, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
 int dec_graph_begin(dec_stream_t stream) {
   if (stream == nullptr) return DEC_E_NULL;
   const hipError_t e =

@@ -18,4 +18,10 @@ hipError_t probe_read_launch(const void* buf, size_t bytes, uint32_t* sink, hipS
 // One workgroup of one wave that does nothing.
 hipError_t probe_empty_launch(hipStream_t stream);
 
+constexpr int kProbeClockSlots = 16;   // clock slots, indexed by XCD id (4 bits)
+
+// kProbeClockSlots workgroups of one wave: each writes its XCD's constant-rate clock to
+// clocks[XCD id].
+hipError_t probe_clock_launch(uint64_t* clocks, hipStream_t stream);
+
 }  // namespace dec

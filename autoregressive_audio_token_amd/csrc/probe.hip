@@ -1,7 +1,8 @@
 // Calibration kernels for the measurements: a plain streaming read, which gives the HBM read
 // bandwidth this part reaches for a given byte count in one launch (the ceiling the attention
-// launch is compared against, beside the 8 TB/s specification), and an empty kernel, which gives
-// the fixed cost of one node of a captured graph.
+// launch is compared against, beside the 8 TB/s specification), an empty kernel, which gives
+// the fixed cost of one node of a captured graph, and a clock reading, which marks points
+// inside a captured graph.
 //
 // The read is shaped as the fastest of the layouts measured for a single ~100 MB launch: every
 // wave reads its own 8 KiB (eight 1 KiB loads, all in flight, 16 bytes per lane), and the grid has
@@ -43,6 +44,16 @@ __global__ __launch_bounds__(kWavesPerGroup * 64) void probe_read_kernel(const u
 
 __global__ __launch_bounds__(64) void probe_empty_kernel() {}
 
+// The dispatcher deals workgroups to the XCDs in turn, so kProbeClockSlots workgroups reach
+// every XCD; each writes that XCD's 100 MHz clock (XCDs keep separate clocks, so a reading
+// is compared only with readings of the same XCD).  Workgroups on one XCD write the same
+// slot within nanoseconds of each other.
+__global__ __launch_bounds__(64) void probe_clock_kernel(uint64_t* clocks) {
+  if (threadIdx.x != 0) return;
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20) & (kProbeClockSlots - 1);
+  clocks[xcc] = __builtin_amdgcn_s_memrealtime();
+}
+
 }  // namespace
 
 hipError_t probe_read_launch(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
@@ -55,6 +66,11 @@ hipError_t probe_read_launch(const void* buf, size_t bytes, uint32_t* sink, hipS
 
 hipError_t probe_empty_launch(hipStream_t stream) {
   hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, stream);
+  return hipGetLastError();
+}
+
+hipError_t probe_clock_launch(uint64_t* clocks, hipStream_t stream) {
+  hipLaunchKernelGGL(probe_clock_kernel, dim3(kProbeClockSlots), dim3(64), 0, stream, clocks);
   return hipGetLastError();
 }
 

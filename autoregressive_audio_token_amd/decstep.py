@@ -64,7 +64,7 @@ _lib = _load()
 # kind[d0,d1,...], whose entries are integer parameters of the same call or literals:
 #   x     element type named by the call's `dtype` (DEC_BF16 bfloat16, DEC_F32 float32)
 #   o     element type named by `out_dtype`;  l  by `logits_dtype`
-#   bf16, f32, i32   that element type;  u32  int32 or uint32 (bit patterns)
+#   bf16, f32, i32   that element type;  u32 / i64  int32 or uint32 / int64 or uint64
 #   bytes            any element type; the shape is a byte count, a lower bound
 # Scalars: int (C int), i32 (int32_t), u64 (uint64_t), float, size (size_t), stream.
 # A trailing "?" gives the Python parameter a default of None.
@@ -144,6 +144,7 @@ _API = {
     "dec_step_advance": "len:i32[B] step:i32[B] B:int stream:stream?",
     "dec_probe_read": "buf:bytes[bytes] bytes:size sink:u32[1] stream:stream?",
     "dec_probe_empty": "stream:stream?",
+    "dec_probe_clock": "clocks:i64[16] stream:stream?",
     "dec_graph_begin": "stream:stream",
     "dec_graph_launch": "exec_handle:int stream:stream?",
 }
@@ -187,8 +188,9 @@ _DECL = {name: _parse(spec) for name, spec in _API.items()}
 def _torch_dtypes():
     import torch
     u32 = (torch.int32,) + ((torch.uint32,) if hasattr(torch, "uint32") else ())
+    u64 = (torch.int64,) + ((torch.uint64,) if hasattr(torch, "uint64") else ())
     return {"bf16": (torch.bfloat16,), "f32": (torch.float32,), "i32": (torch.int32,),
-            "u32": u32, DEC_BF16: (torch.bfloat16,), DEC_F32: (torch.float32,)}
+            "u32": u32, "i64": u64, DEC_BF16: (torch.bfloat16,), DEC_F32: (torch.float32,)}
 
 
 _DTYPES = _torch_dtypes()

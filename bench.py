@@ -7,8 +7,9 @@ for all layers (one fused launch), then the fused top-k sampler over the 9
 codebooks.  Exactly --warmup untimed and --steps timed steps run, each on the
 next of R cache sets in rotation; the sets are distinct allocations, so each
 step reads cold data (R x valid bytes exceeds the 256 MB Infinity Cache).  The
-timed steps run as min(10, steps) captured hipGraphs of near-equal size, with
-HIP events between them (per-block step times beside the total).
+timed steps run as one captured hipGraph timed with HIP events; clock-reading
+nodes inside it split them into min(10, steps) blocks (per-block step times
+beside the total).
 
 Prints ONE JSON line: value = valid K/V bytes per step / time per step (GB/s).
 
@@ -633,7 +634,7 @@ def main(argv=None):
     plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k or model)
     all_cores = None
     if not a.no_cpu_baseline:  # its worker processes are forked before any GPU call
-        log("timing the oracle on all host cores")
+        print("[bench] timing the oracle on all host cores", file=sys.stderr, flush=True)
         all_cores = cpu_baseline_all_cores(w, a.cpu_seconds)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -766,57 +767,58 @@ def main(argv=None):
         return 0
     # Exactly `warmup` untimed steps, then exactly `steps` timed ones, each step on the next
     # cache set in rotation (no set is read twice within R steps, so a step finds its K/V
-    # bytes in HBM, not in a cache).  The timed steps run as min(10, steps) captured graphs
-    # of near-equal size with an event between graphs: the per-block step times come from
-    # those events, `value` from the first and last.  The warm-up runs in graphs of the
-    # same size.  Graphs are keyed by (first set, steps), so equal blocks share one.
-    graphs = {}
-
-    def block_graph(first, n):
-        key = (first % R, n)
-        if key not in graphs:
-            with torch.cuda.stream(stream):
-                dec.dec_graph_begin(stream)
-                for j in range(n):
-                    attn(sets[(first + j) % R], stream)
-                    sample(stream)
-                graphs[key] = dec.dec_graph_end(stream)
-        return graphs[key]
-
+    # bytes in HBM, not in a cache).  Each runs as one captured graph.  Inside the timed
+    # graph, dec_probe_clock nodes mark the edges of min(10, steps) blocks of near-equal size
+    # (one node each); the per-block step times come from one XCD's clock.  `value` comes
+    # from HIP events around the timed graph's launch.
     def split(total, parts):
         q, r = divmod(total, parts)
         return [q + 1] * r + [q] * (parts - r)
 
+    def capture(first, sizes, clocks=None):
+        with torch.cuda.stream(stream):
+            dec.dec_graph_begin(stream)
+            pos = first
+            if clocks is not None:
+                dec.dec_probe_clock(clocks[0], stream)
+            for i, n in enumerate(sizes):
+                for _ in range(n):
+                    attn(sets[pos % R], stream)
+                    sample(stream)
+                    pos += 1
+                if clocks is not None:
+                    dec.dec_probe_clock(clocks[i + 1], stream)
+            return dec.dec_graph_end(stream)
+
     steps = a.steps
     n_blocks = min(10, steps)
     timed = split(steps, n_blocks)
-    warm = split(a.warmup, -(-a.warmup // max(timed))) if a.warmup > 0 else []
-    plan, pos = [], 0
-    for n in warm + timed:
-        plan.append(block_graph(pos, n))
-        pos += n
+    clocks = torch.zeros((n_blocks + 1, 16), dtype=torch.int64, device=dev)
+    warm_graph = capture(0, [a.warmup]) if a.warmup > 0 else None
+    timed_graph = capture(a.warmup, timed, clocks)
     with torch.cuda.stream(stream):
         dec.dec_attn_workspace_init(ws, nb, stream)
-    log(f"{R} cache sets, {len(graphs)} graphs captured; {a.warmup} warm-up and {steps} timed "
-        f"steps in {len(warm)} + {n_blocks} graphs")
-    for g in plan[:len(warm)]:
-        dec.dec_graph_launch(g, stream)
+    log(f"{R} cache sets; {a.warmup} warm-up and {steps} timed steps captured ({n_blocks} "
+        f"blocks)")
+    if warm_graph is not None:
+        dec.dec_graph_launch(warm_graph, stream)
     stream.synchronize()
     torch.cuda.synchronize()
-    evs_blk = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    evs_blk[0].record(stream)
-    for i, g in enumerate(plan[len(warm):]):
-        dec.dec_graph_launch(g, stream)
-        evs_blk[i + 1].record(stream)
+    e_start.record(stream)
+    dec.dec_graph_launch(timed_graph, stream)
+    e_end.record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = evs_blk[0].elapsed_time(evs_blk[-1]) / steps
-    blk_us = sorted(evs_blk[i].elapsed_time(evs_blk[i + 1]) * 1e3 / timed[i]
-                    for i in range(n_blocks))
-    for g in graphs.values():
-        dec.dec_graph_destroy(g)
+    ms_per_step = e_start.elapsed_time(e_end) / steps
+    ck = clocks.cpu().numpy()
+    xcd = next(x for x in range(ck.shape[1]) if np.all(ck[:, x] > 0))  # one XCD's clock
+    blk_us = sorted(float(ck[i + 1, xcd] - ck[i, xcd]) * 0.01 / timed[i] for i in range(n_blocks))
+    for g in (warm_graph, timed_graph):
+        if g is not None:
+            dec.dec_graph_destroy(g)
     out_ok = bool(torch.isfinite(o_s).all().item() and torch.isfinite(o_c).all().item())
     tok_h = tok.cpu().numpy()
     tok_ok = bool(np.all((tok_h >= 0) & (tok_h < w.vocab_valid) | (tok_h == w.fill_token)))
@@ -893,7 +895,9 @@ def main(argv=None):
         "us_per_step": round(ms_per_step * 1e3, 3),
         "us_per_step_blocks": {"blocks": n_blocks, "steps_per_block": [min(timed), max(timed)],
                                "median": round(blk_us[len(blk_us) // 2], 3),
-                               "min": round(blk_us[0], 3), "max": round(blk_us[-1], 3)},
+                               "min": round(blk_us[0], 3), "max": round(blk_us[-1], 3),
+                               "clock": f"XCD {xcd}'s 100 MHz clock, read by dec_probe_clock "
+                                        f"nodes at the block edges inside the timed graph"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -909,9 +913,9 @@ def main(argv=None):
             "static_cache_bytes_per_set": static_bytes,
             "kv_layout": (f"self cache paged, {a.paged} keys per block" if a.paged
                           else "static caches"),
-            "schedule": (f"model-shaped: one hipGraph per timed block; step = {attn_entry} "
+            "schedule": (f"model-shaped: the timed steps as one hipGraph; step = {attn_entry} "
                          f"({attn_launches} launches) + {samp_entry}" if model else
-                         f"one hipGraph per timed block; step = {attn_entry} (self+cross, "
+                         f"the timed steps as one hipGraph; step = {attn_entry} (self+cross, "
                          f"all layers, one launch) + {samp_entry}"),
             "variant": {"head_dim": w.head_dim, "cross_mask": mask_note,
                         "attention_outputs": "bf16" if a.out_bf16 else "f32",

@@ -415,6 +415,16 @@ int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);
 int dec_probe_read(const void* buf, size_t bytes, uint32_t* sink, dec_stream_t stream);
 int dec_probe_empty(dec_stream_t stream);
 
+/* Calibration too: marks a point in a stream or a captured graph.  Launches
+ * DEC_PROBE_CLOCK_SLOTS single-wave workgroups; the dispatcher deals them to the
+ * XCDs in turn, and each writes its XCD's constant-rate clock (100 MHz, 10 ns per
+ * tick) to clocks[XCD id].  clocks: DEC_PROBE_CLOCK_SLOTS uint64 entries, device,
+ * 8-byte aligned (else DEC_E_NULL / DEC_E_ALIGN); entries of XCDs that ran no
+ * workgroup keep their value.  XCDs keep separate clocks, offset by microseconds:
+ * compare a slot only with the same slot of other readings. */
+#define DEC_PROBE_CLOCK_SLOTS 16
+int dec_probe_clock(uint64_t* clocks, dec_stream_t stream);
+
 /* Graph capture of a whole decode step ("Analysis and improvements": the step
  * is captured once and replayed with a single launch).  begin/end bracket
  * ordinary dec_* calls on a non-default stream; end returns an executable

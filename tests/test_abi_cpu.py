@@ -479,7 +479,8 @@ def _good_call(params):
     """CPU tensors and integers that satisfy every declaration of one entry point."""
     import torch
     dt = {"x": torch.bfloat16, "o": torch.float32, "l": torch.bfloat16, "bf16": torch.bfloat16,
-          "f32": torch.float32, "i32": torch.int32, "u32": torch.int32, "bytes": torch.uint8}
+          "f32": torch.float32, "i32": torch.int32, "u32": torch.int32, "i64": torch.int64,
+          "bytes": torch.uint8}
     ints = {n: v for n, v in _SIZES.items()}
     ints.update(dtype=D.DEC_BF16, out_dtype=D.DEC_F32, logits_dtype=D.DEC_BF16)
     args = {}

@@ -107,3 +107,20 @@ def test_oracle_baseline_on_all_cores_runs_whole_steps_in_worker_processes():
     s_len, c_len = gen.lengths(configs.TINY)
     valid = configs.valid_kv_bytes(configs.TINY, s_len, c_len)
     assert abs(r["value"] - valid / (r["us_per_step"] * 1e-6) / 1e9) <= 1e-3 * r["value"] + 1e-4
+
+
+def test_the_default_path_reaches_the_gpu_step_on_a_host_without_one(monkeypatch):
+    # everything main() does before its first GPU call (argument checks, the all-cores
+    # oracle baseline) runs on the CPU; the GPU step is stubbed to stop there
+    import torch
+    from workloads import configs
+    calls = []
+    monkeypatch.setattr(bench, "cpu_baseline_all_cores",
+                        lambda w, s: calls.append(w.name) or {"value": 1.0})
+
+    def stop(dev):
+        raise RuntimeError("reached the GPU step")
+    monkeypatch.setattr(torch.cuda, "set_device", stop)
+    with pytest.raises(RuntimeError, match="reached the GPU step"):
+        bench.main(["--workload", "tiny", "--cpu-seconds", "0"])
+    assert calls == [configs.TINY.name]

@@ -52,3 +52,31 @@ def test_two_magic_words_in_one_lane_cancel_and_nothing_past_the_range_is_read()
 def test_empty_kernel_runs():
     dec.dec_probe_empty()
     torch.cuda.synchronize()
+
+
+def test_clock_readings_bracket_the_work_between_them():
+    # dec_probe_clock before and after a 1 GiB streaming read: on every XCD that recorded
+    # both readings the difference is the read's duration (HIP events around the same work
+    # bracket it, with the clocks' 10 ns ticks), and the readings fill at least 4 XCD slots
+    n = 1 << 30
+    buf = torch.zeros(n, dtype=torch.uint8, device=hp.DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=hp.DEV)
+    c0 = torch.zeros(16, dtype=torch.int64, device=hp.DEV)
+    c1 = torch.zeros(16, dtype=torch.int64, device=hp.DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dec.dec_probe_read(buf, n, sink)               # warm
+    torch.cuda.synchronize()
+    e0.record()
+    dec.dec_probe_clock(c0)
+    dec.dec_probe_read(buf, n, sink)
+    dec.dec_probe_clock(c1)
+    e1.record()
+    torch.cuda.synchronize()
+    a, b = c0.cpu().numpy(), c1.cpu().numpy()
+    both = (a > 0) & (b > 0)
+    print(f"[clock] slots {np.nonzero(both)[0].tolist()}", flush=True)
+    assert both.sum() >= 4
+    ev_us = e0.elapsed_time(e1) * 1e3
+    for x in np.nonzero(both)[0]:
+        us = (int(b[x]) - int(a[x])) * 0.01
+        assert 0.5 * ev_us - 20 <= us <= ev_us + 1, (int(x), us, ev_us)
