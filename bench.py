@@ -78,12 +78,18 @@ def parse(argv=None):
     ap.add_argument("--separate-append", action="store_true",
                     help="with --decode-loop: append the current token's rows with\n"
                          "dec_kv_append as a node of its own (for comparison)")
+    ap.add_argument("--attn-chunk", type=int, default=0, metavar="KEYS",
+                    help="keys per split-K chunk of every attention launch (a power of two,\n"
+                         "128-1024; 0: the launcher chooses), through dec_tuning_set")
     ap.add_argument("--calibrate", action="store_true",
                     help="the calibration kernels: streaming reads at 4 MiB, the workload's\n"
                          "valid bytes and 4 GiB, and the cost of an empty graph node")
     a = ap.parse_args(argv)
     if a.steps < 1 or a.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
+    if a.attn_chunk and (a.attn_chunk < 128 or a.attn_chunk > 1024 or
+                         a.attn_chunk & (a.attn_chunk - 1)):
+        ap.error("--attn-chunk must be a power of two from 128 to 1024")
     return a
 
 
@@ -631,7 +637,10 @@ def main(argv=None):
     if model and (ex_attn or a.paged):
         print("--schedule model goes with the static caches and fp32 outputs", file=sys.stderr)
         return 2
-    plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k or model)
+    plain = not (ex_attn or ex_samp or a.paged or a.head_dim != 64 or a.top_k or model or
+                 a.attn_chunk)
+    if a.attn_chunk:
+        dec.dec_tuning_set(attn_chunk_keys=a.attn_chunk)
     all_cores = None
     if not a.no_cpu_baseline:  # its worker processes are forked before any GPU call
         print("[bench] timing the oracle on all host cores", file=sys.stderr, flush=True)
@@ -919,7 +928,8 @@ def main(argv=None):
                          f"all layers, one launch) + {samp_entry}"),
             "variant": {"head_dim": w.head_dim, "cross_mask": mask_note,
                         "attention_outputs": "bf16" if a.out_bf16 else "f32",
-                        "logits": "bf16" if a.logits_bf16 else "f32", "top_k": top_k},
+                        "logits": "bf16" if a.logits_bf16 else "f32", "top_k": top_k,
+                        "attn_chunk_keys": a.attn_chunk or "chosen per launch"},
         },
         "roofline": {
             "bound": "hbm",

@@ -124,3 +124,10 @@ def test_the_default_path_reaches_the_gpu_step_on_a_host_without_one(monkeypatch
     with pytest.raises(RuntimeError, match="reached the GPU step"):
         bench.main(["--workload", "tiny", "--cpu-seconds", "0"])
     assert calls == [configs.TINY.name]
+
+
+def test_attention_chunk_option_parses():
+    assert bench.parse(["--attn-chunk", "256"]).attn_chunk == 256
+    for bad in ("100", "2048", "96"):
+        with pytest.raises(SystemExit):
+            bench.parse(["--attn-chunk", bad])
