@@ -183,11 +183,11 @@ int attn_common(const SegArgs* segs, int nseg, int NL, int B, int H, int hd, int
   const WsLayout& lay = small_ok ? lay_min : lay_max;
   const int min_log2 = dec::attn_log2(small_ok ? dec::kAttnMinChunk : dec::kAttnChunk);
   int chunk_log2 = 0;  // the launcher chooses
-  const int chunk_env = g_tuning.attn_chunk_keys;
-  if (chunk_env != 0) {  // a fixed chunk (tests of every cut)
-    if (!is_pow2(chunk_env) || chunk_env > dec::kAttnChunk || chunk_env < (1 << min_log2))
+  const int chunk_keys = g_tuning.attn_chunk_keys;
+  if (chunk_keys != 0) {  // a fixed chunk (tests of every cut, measurements)
+    if (!is_pow2(chunk_keys) || chunk_keys > dec::kAttnChunk || chunk_keys < (1 << min_log2))
       return DEC_E_UNSUPPORTED;
-    chunk_log2 = dec::attn_log2(chunk_env);
+    chunk_log2 = dec::attn_log2(chunk_keys);
   }
 
   dec::AttnParams p{};
