@@ -74,6 +74,10 @@ def test_abi_host_code_under_address_and_undefined_behaviour_sanitizers():
     rt = _runtime()
     if rt is None:
         pytest.skip("no clang sanitizer runtime")
+    try:
+        B.hipcc_path()
+    except RuntimeError:
+        pytest.skip("no hipcc")
     lib = _build()
     syms = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout
     assert "__asan_init" in syms and "__ubsan_handle" in syms, "the library is not instrumented"
