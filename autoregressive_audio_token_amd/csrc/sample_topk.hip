@@ -21,21 +21,27 @@
 //      are never kept.  The survivors (typically under a tenth of the row) are
 //      compacted through LDS, still in vocabulary order, to at most kSurvSlots
 //      per lane; if more survive, the full row is searched instead.
-//   3. Exact threshold: MSB-first bisection for the kk-th largest key; each step
-//      counts keys >= candidate with wave ballots and stops once exactly kk
-//      remain.  Keys above it are kept, plus the lowest-index keys equal to it;
-//      ranks in vocabulary order come from ballots and mbcnt, and the kept
-//      entries are compacted through LDS so lane t holds the t-th kept entry in
-//      ascending vocabulary order (kk <= 64).
-//   4. e_t = exp((x_t - max) / T); wave inclusive scan; C_t = S_t / S_last;
-//      the token is the first kept entry with u < C_t.  T <= 0: greedy.
+//   3. Exact threshold: a radix search for the kk-th largest key, 8 bits per
+//      pass (a 256-bucket LDS histogram of the keys that still match the
+//      resolved prefix, a wave scan and a ballot), stopping once exactly kk keys
+//      reach the prefix.  Keys above it are kept, plus the lowest-index keys
+//      equal to it; ranks in vocabulary order come from ballots and mbcnt, and
+//      the kept entries are compacted through LDS so lane t holds the t-th kept
+//      entry in ascending vocabulary order (kk <= 64).
+//   4. e_t = exp((x_t - max) / T) and their sum in float64; p_t = e_t / sum,
+//      rounded once to float32 (the exported probability); the CDF is the
+//      float64 running sum of those p_t, and the token is the first kept entry
+//      with u < C_t (the last one if rounding leaves u >= C_last).  T <= 0:
+//      greedy.
 //
-// Wide variant (top_k > 64): no pruning (the lane maxima bound only the 64th
-// largest key); the radix search runs over the whole row, and the kept entries
-// stay where they were loaded.  Slot j of every lane holds vocabulary entries
-// 64 j .. 64 j + 63, so the CDF in vocabulary order is one wave scan per slot
-// plus the running total of the slots before it.  Logits may be bf16: each
-// value widens exactly to fp32 before its key is formed.
+// Wide variant (top_k > 64): the lane maxima bound only the 64th largest key,
+// so up to top_k 256 a wider bound prunes the row (the WIDE branch below); the
+// radix search then runs over the compacted survivors, or over the whole row.
+// The kept entries stay where they were loaded: slot j of every lane holds
+// entries 64 j .. 64 j + 63 (of the row or of its survivors, in vocabulary
+// order), so the CDF in vocabulary order is one wave scan per slot plus the
+// running total of the slots before it.  Logits may be bf16: each value widens
+// exactly to fp32 before its key is formed.
 #include "dec_common.h"
 #include "dec_kernels.h"
 
