@@ -15,8 +15,8 @@
 //     keys, 1 KiB, fully coalesced; at head dim 128 a tile is 16 keys of 256 B,
 //     the same bytes), and the next tile's K and V loads are in flight while
 //     the current tile is computed (double buffering).  Tiles of this size keep
-//     the kernel at three waves per SIMD.  There is no MFMA: the work is a
-//     GEMV, bound by HBM.
+//     the bf16 static kernel at four waves per SIMD (128 VGPRs) and the other
+//     variants at three.  There is no MFMA: the work is a GEMV, bound by HBM.
 //   * Scores reduce across the 8 lanes of a key with DPP moves.  Each group of
 //     8 lanes keeps its own online-softmax state across the tiles (base 2, q
 //     pre-scaled by scale * log2 e, fp32), so a tile needs no cross-lane max.
@@ -36,6 +36,12 @@
 //     each).  The work list is derived on the device from len[] (device
 //     resident, so a captured graph stays valid as lengths change), longest
 //     sequences first; a persistent, occupancy-sized grid walks it.
+//   * A launch whose sequences each get one workgroup cuts the excess of its
+//     heaviest sequences (beyond a multiple of the CU count) in halves, so every
+//     CU carries nearly the same bytes.
+//   * Each wave records in the workspace the tile it read first; the next launch
+//     on the workspace requests that tile into LDS before deriving its schedule
+//     and uses it only when its own first tile is the same one.
 
 #include "dec_common.h"
 #include "dec_kernels.h"
