@@ -693,9 +693,10 @@ int dec_tuning_set(const dec_tuning* t) {
   if (ck != 0 && (!is_pow2(ck) || ck < 128 || ck > dec::kAttnChunk)) return DEC_E_SHAPE;
   if (t->attn_schedule < 0 || t->attn_schedule > 2 || t->attn_blocks < 0 ||
       t->attn_no_halves < 0 || t->attn_no_halves > 1 || t->attn_no_records < 0 ||
-      t->attn_no_records > 1 || t->head_kernel < 0 || t->head_kernel > 2 ||
-      t->head_mfma_cfg < 0 || t->head_mfma_cfg > 99)
+      t->attn_no_records > 1 || t->head_kernel < 0 || t->head_kernel > 2)
     return DEC_E_SHAPE;
+  const int mc = t->head_mfma_cfg;  // the MFMA kernel's instantiated tilings
+  if (mc != 0 && mc != 11 && mc != 12 && mc != 22 && mc != 42) return DEC_E_SHAPE;
   g_tuning = *t;
   return DEC_OK;
 }

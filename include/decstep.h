@@ -449,8 +449,8 @@ int dec_graph_destroy(void* exec);
  *   attn_no_records  1: launches do not request the tiles recorded by the last launch
  *   head_kernel      0: by shape; 1: the vector-ALU kernel at every batch size; 2: the
  *                    MFMA kernel wherever its alignment allows
- *   head_mfma_cfg    0: the measured policy; else 10 * row tiles + batch tiles per
- *                    workgroup of the MFMA kernel
+ *   head_mfma_cfg    0: the measured policy; else the MFMA kernel's tiling per
+ *                    workgroup as 10 * row tiles + batch tiles: 11, 12, 22 or 42
  * dec_tuning_set(NULL) restores the defaults.  Returns DEC_E_SHAPE for a value out of
  * range (nothing is changed). */
 typedef struct dec_tuning {

@@ -385,6 +385,64 @@ def test_misc_validation():
     assert D.raw_status("dec_probe_read", A, 16, A + 2, None) == D.DEC_E_ALIGN
 
 
+def test_tuning_overrides_round_trip_refuse_out_of_range_and_reset():
+    before = dec.dec_tuning_get()
+    try:
+        dec.dec_tuning_set()
+        assert all(v == 0 for v in dec.dec_tuning_get().values())
+        good = dict(attn_chunk_keys=256, attn_schedule=2, attn_blocks=77, attn_no_halves=1,
+                    attn_no_records=1, head_kernel=2, head_mfma_cfg=22)
+        dec.dec_tuning_set(**good)
+        assert dec.dec_tuning_get() == good
+        bad = ([dict(attn_chunk_keys=c) for c in (-128, 64, 100, 384, 2048)] +
+               [dict(attn_schedule=v) for v in (-1, 3)] + [dict(attn_blocks=-1)] +
+               [dict(attn_no_halves=v) for v in (-1, 2)] +
+               [dict(attn_no_records=v) for v in (-1, 2)] +
+               [dict(head_kernel=v) for v in (-1, 3)] +
+               [dict(head_mfma_cfg=v) for v in (-1, 1, 13, 21, 33, 41, 44, 99, 100)])
+        for fields in bad:
+            with pytest.raises(D.DecError) as err:
+                dec.dec_tuning_set(**fields)
+            assert err.value.status == D.DEC_E_SHAPE, fields
+            assert dec.dec_tuning_get() == good, fields  # a refused call changes nothing
+        for c in (11, 12, 22, 42):  # every instantiated tiling of the MFMA head
+            dec.dec_tuning_set(head_mfma_cfg=c)
+            assert dec.dec_tuning_get()["head_mfma_cfg"] == c
+        for c in (128, 512, 1024):
+            dec.dec_tuning_set(attn_chunk_keys=c)
+            assert dec.dec_tuning_get()["attn_chunk_keys"] == c
+        with pytest.raises(TypeError):
+            dec.dec_tuning_set(no_such_field=1)
+        dec.dec_tuning_set()
+        assert all(v == 0 for v in dec.dec_tuning_get().values())
+        assert D.raw_status("dec_tuning_get", None) == D.DEC_E_NULL
+    finally:
+        dec.dec_tuning_set(**before)
+
+
+def test_tuning_overrides_belong_to_the_calling_thread():
+    import threading
+    before = dec.dec_tuning_get()
+    seen = {}
+
+    def other():
+        seen["start"] = dec.dec_tuning_get()
+        dec.dec_tuning_set(attn_blocks=5)
+        seen["after"] = dec.dec_tuning_get()
+
+    try:
+        dec.dec_tuning_set(attn_schedule=1, head_kernel=1)
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+        assert all(v == 0 for v in seen["start"].values())  # a new thread starts at defaults
+        assert seen["after"]["attn_blocks"] == 5
+        mine = dec.dec_tuning_get()  # the other thread's setting never reaches this one
+        assert (mine["attn_schedule"], mine["head_kernel"], mine["attn_blocks"]) == (1, 1, 0)
+    finally:
+        dec.dec_tuning_set(**before)
+
+
 def test_order_key_map_is_monotone_over_all_float32_bit_patterns():
     # Every float32 bit pattern, in increasing order of value: -inf .. -0 then +0 .. +inf.
     # Keys must increase strictly, except that -0 and +0 share a key; NaNs map outside
