@@ -716,7 +716,7 @@ const char* dec_strerror(int status) {
     case DEC_E_SHAPE: return "DEC_E_SHAPE: a size is out of range or sizes disagree";
     case DEC_E_DTYPE: return "DEC_E_DTYPE: unknown dtype code";
     case DEC_E_WORKSPACE: return "DEC_E_WORKSPACE: workspace too small";
-    case DEC_E_UNSUPPORTED: return "DEC_E_UNSUPPORTED: case not implemented (e.g. head_dim != 64)";
+    case DEC_E_UNSUPPORTED: return "DEC_E_UNSUPPORTED: a legal but unimplemented case (e.g. head_dim other than 64 or 128)";
     case DEC_E_HIP: return "DEC_E_HIP: a HIP runtime call failed (see dec_last_hip_error)";
     case DEC_E_ALIGN: return "DEC_E_ALIGN: pointer not aligned as required";
     default: return "unknown dec_status";
