@@ -197,9 +197,10 @@ int dec_attn_step_noalloc(const void* q_self, const void* k_self, const void* v_
  *               set = key j attended.  Keys j < enc_len[b] with their bit set
  *               take part; a row with none outputs zeros.  mask_words must be
  *               even and at least 2 * ceil(L_cap_cross / 64) (a tile reads the
- *               whole words that hold its keys' bits); 8-byte aligned.  A tile with no attended key is not read; the
- *               other keys of a tile that has one are read and weighted zero, so
- *               masked keys below enc_len[b] must hold finite values.
+ *               whole words that hold its keys' bits); 8-byte aligned.  A tile
+ *               with no attended key is not read; the other keys of a tile that
+ *               has one are read and weighted zero, so masked keys below
+ *               enc_len[b] must hold finite values.
  *   out_dtype   DEC_F32 (float outputs, as dec_attn_step) or DEC_BF16 (outputs
  *               rounded to bfloat16, nearest-even, from the same fp32 values;
  *               out pointers 2-byte aligned).
