@@ -47,6 +47,13 @@
 
 namespace dec {
 
+// Entry slots per lane that every row given to the VPL-slot instantiation fills on every lane:
+// sample_launch picks the smallest VPL in {4, 8, 16, 18, 32, 64} that covers the row, so the
+// row is longer than the next smaller size's slots.
+constexpr int samp_full_slots(int vpl) {
+  return vpl == 8 ? 4 : vpl == 16 ? 8 : vpl == 18 ? 16 : vpl == 32 ? 18 : vpl == 64 ? 32 : 0;
+}
+
 constexpr int kSurvSlots = 3;                   // survivor slots per lane after pruning
 constexpr int kSurvCap = kSurvSlots * kWave;     // survivors that fit
 // Wide variant: top_k up to kWidePruneK is pruned to at most kWideSlots per lane (the
@@ -339,20 +346,24 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     u = p.uniforms[row];
   }
 
+  // Slots below samp_full_slots(VPL) hold valid entries on every lane (the launcher picks VPL
+  // only for rows longer than that many slots), so they load at fixed offsets from one base,
+  // with no clamp and no mask; the others clamp their index, so every load stays in the row.
+  constexpr int kFull = samp_full_slots(VPL);
   const LT* x = static_cast<const LT*>(p.logits) + (size_t)row * p.V_stride;
   float v[VPL];
   uint32_t key[VPL];
   int idx[VPL];
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) {  // clamped index: every load is in bounds, no branches
+  for (int j = 0; j < VPL; ++j) {  // no branches
     const int i = j * kWave + lane;
-    v[j] = logit_at(x, i < p.V_valid ? i : p.V_valid - 1);
+    v[j] = logit_at(x, j < kFull || i < p.V_valid ? i : p.V_valid - 1);
   }
   uint32_t lmax = 0u;
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int i = j * kWave + lane;
-    const bool ok = i < p.V_valid;
+    const bool ok = j < kFull || i < p.V_valid;
     key[j] = order_key(v[j]) & (ok ? 0xFFFFFFFFu : 0u);  // absent: below every candidate
     idx[j] = ok ? i : -1;
     lmax = key[j] > lmax ? key[j] : lmax;
@@ -503,6 +514,8 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
 
 template <int VPL>
 static hipError_t sample_launch_vpl(const SampleParams& p, hipStream_t stream) {
+  // the kernel reads slots below samp_full_slots(VPL) without a bound: the row must be longer
+  if (p.V_valid <= samp_full_slots(VPL) * kWave || p.V_valid > VPL * kWave) return hipErrorInvalidValue;
   const int rows = p.B * p.n_cb;
   const dim3 grid((rows + kSampWaves - 1) / kSampWaves), block(kSampWaves * kWave);
   const bool wide = p.top_k > kSampNarrowK;
