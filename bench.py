@@ -695,15 +695,15 @@ def main(argv=None):
         # lives in physical block table[b, i]; the pool holds one spare block per sequence
         bs = a.paged
         mb = w.self_cap // bs
-        n_blocks = w.batch * (mb + 1)
-        perm = np.random.default_rng(12345).permutation(n_blocks)[:w.batch * mb]
+        pool_blocks = w.batch * (mb + 1)
+        perm = np.random.default_rng(12345).permutation(pool_blocks)[:w.batch * mb]
         table_h = perm.reshape(w.batch, mb).astype(np.int32)
         table = torch.from_numpy(table_h).to(dev)
         idx = torch.from_numpy(table_h.reshape(-1)).to(dev).long()
         for st in sets:
             for which in ("k_self", "v_self"):
                 src = st[which]                       # [NL, B, H, L_cap, hd]
-                pool = torch.full((w.n_layers, n_blocks, w.heads, bs, w.head_dim), float("nan"),
+                pool = torch.full((w.n_layers, pool_blocks, w.heads, bs, w.head_dim), float("nan"),
                                   dtype=src.dtype, device=dev)
                 blocks = src.view(w.n_layers, w.batch, w.heads, mb, bs, w.head_dim)
                 blocks = blocks.permute(0, 1, 3, 2, 4, 5).reshape(
@@ -715,7 +715,7 @@ def main(argv=None):
     def attn(st, s):
         if ex_attn and a.paged:          # a paged self cache with the widenings
             dec.dec_attn_step_paged_ex(d["q_self"], st["k_self"], st["v_self"], table, d["len"],
-                                       a.paged, n_blocks, w.self_cap // a.paged, o_s,
+                                       a.paged, pool_blocks, w.self_cap // a.paged, o_s,
                                        d["q_cross"], st["k_cross"], st["v_cross"], d["enc_len"],
                                        mask_d, mask_words, w.cross_cap, o_c, w.n_layers, w.batch,
                                        w.heads, w.head_dim, code,
@@ -740,7 +740,7 @@ def main(argv=None):
             return
         if a.paged:
             dec.dec_attn_step_paged(d["q_self"], st["k_self"], st["v_self"], table, d["len"],
-                                    a.paged, n_blocks, w.self_cap // a.paged, o_s, d["q_cross"],
+                                    a.paged, pool_blocks, w.self_cap // a.paged, o_s, d["q_cross"],
                                     st["k_cross"], st["v_cross"], d["enc_len"], w.cross_cap, o_c,
                                     w.n_layers, w.batch, w.heads, w.head_dim, code, w.scale, ws,
                                     nb, s)
