@@ -37,9 +37,9 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Butterfly across lanes that differ in bit positions [log2(FROM), 6): combines the
 // values held by lanes lane ^ FROM, lane ^ 2*FROM, ... (all lanes end with the result).
-// (The gfx950 permlane16/32 swaps would do the 16- and 32-lane steps in one VALU
-// op, but this compiler folds their two results as equal when both inputs are the
-// same value, so the steps use shuffles.)
+// (The gfx950 permlane16/32 swaps do the 16- and 32-lane steps in one VALU op each,
+// bit for bit the same; in the attention kernel they measured slower than these
+// shuffles, the compiler then holding more scalar state in lanes of VGPRs.)
 template <int FROM>
 __device__ __forceinline__ float xor_max_from(float v) {
   if constexpr (FROM <= 8) v = fmaxf(v, dpp_f32<kDppRowRor8>(v));
