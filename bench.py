@@ -130,8 +130,8 @@ def decode_loop(a):
     token's key and value rows and attends over s + 1 self keys (and the description) in
     one launch, then samples with Philox uniforms drawn from (seed, step) and the delay mask
     and advances the lengths and steps in the sampler's own launch: two graph nodes per
-    step.  Graphs of R steps (one per cache set) are replayed n_steps / R times and timed
-    end to end."""
+    step.  The whole generation is one captured graph, its steps on R cache sets in turn,
+    timed end to end."""
     import numpy as np
     import torch
     import autoregressive_audio_token_amd as dec
@@ -154,9 +154,6 @@ def decode_loop(a):
     d = wdev.step_inputs(w, dev, self_lens=np.ones(B, np.int32), cross_lens=c_len,
                          fill_lens=fill)
     R = a.sets if a.sets > 0 else 8
-    if S % R:
-        print(f"--sets must divide the {S} steps", file=sys.stderr)
-        return 2
     big = ("k_self", "v_self", "k_cross", "v_cross")
     sets = [{k: d[k] for k in big}]
     for _ in range(R - 1):
@@ -199,20 +196,18 @@ def decode_loop(a):
 
     with torch.cuda.stream(stream):
         dec.dec_attn_workspace_init(ws, nb, stream)
-        dec.dec_graph_begin(stream)
-        for st in sets:
-            step(st, stream)
+        dec.dec_graph_begin(stream)             # the whole generation as one graph
+        for s in range(S):
+            step(sets[s % R], stream)
         graph = dec.dec_graph_end(stream)
         reset()
-        for _ in range(S // R):                 # one untimed generation
-            dec.dec_graph_launch(graph, stream)
+        dec.dec_graph_launch(graph, stream)     # one untimed generation
         reset()
     stream.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"{R}-step graph captured; timing {S} steps")
+    log(f"{S}-step graph captured ({R} cache sets in turn); timing it")
     e0.record(stream)
-    for _ in range(S // R):
-        dec.dec_graph_launch(graph, stream)
+    dec.dec_graph_launch(graph, stream)
     e1.record(stream)
     stream.synchronize()
     total_ms = e0.elapsed_time(e1)
@@ -237,15 +232,15 @@ def decode_loop(a):
                    "self_cap": w.self_cap, "cross_len": [int(x) for x in c_len][:4],
                    "cross_cap": w.cross_cap, "top_k": w.top_k, "cache_sets": R,
                    "valid_kv_bytes_total": int(total_bytes),
-                   "schedule": (f"decode loop: graphs of {R} steps (dec_kv_append, "
-                                f"dec_attn_step, dec_sample_topk_advance: three nodes; one "
-                                f"cache set per step) replayed {S // R} times"
+                   "schedule": (f"decode loop: one graph of {S} steps (dec_kv_append, "
+                                f"dec_attn_step, dec_sample_topk_advance: three nodes per "
+                                f"step; the steps on {R} cache sets in turn)"
                                 if a.separate_append else
-                                f"decode loop: graphs of {R} steps (dec_attn_step_append: "
+                                f"decode loop: one graph of {S} steps (dec_attn_step_append: "
                                 f"the current token's rows appended and attended in one "
                                 f"launch; dec_sample_topk_advance: sampling and the length "
-                                f"and step advance in one launch; one cache set per step) "
-                                f"replayed {S // R} times")},
+                                f"and step advance in one launch; the steps on {R} cache "
+                                f"sets in turn)")},
         "total_ms": round(total_ms, 3),
         "total_ms_at_70pct_of_peak": round(total_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 3),
         "roofline": {"bound": "hbm", "kernel": "whole step (append + attention, sampler + advance)",
