@@ -219,4 +219,11 @@ struct AppendParams {
 hipError_t append_launch(const AppendParams& p, hipStream_t stream);
 hipError_t advance_launch(int32_t* len, int32_t* step, int B, hipStream_t stream);
 
+// ---- uniforms of several steps in one launch -----------------------------------------
+
+// out[(s * B + b) * n_cb + c] = the Philox4x64-10 uniform of row (b, c) at step step0 + s
+// (the value the sampler draws for that row and step); total = n_steps * B * n_cb.
+hipError_t uniforms_launch(uint64_t seed, int step0, int B, int n_cb, int total, float* out,
+                           hipStream_t stream);
+
 }  // namespace dec

@@ -616,6 +616,18 @@ int dec_embed_sum(const int32_t* tokens, const void* E, float* x, int B, int n_c
   return e == hipSuccess ? DEC_OK : hip_fail(e);
 }
 
+int dec_philox_uniforms(uint64_t seed, int step0, int n_steps, int B, int n_cb, float* out,
+                        dec_stream_t stream) {
+  if (out == nullptr) return DEC_E_NULL;
+  if (n_steps < 1 || B < 1 || n_cb < 1 || step0 < 0) return DEC_E_SHAPE;
+  if ((long long)step0 + n_steps > 0x7FFFFFFFLL || (long long)n_steps * B * n_cb > 0x7FFFFFFFLL)
+    return DEC_E_SHAPE;
+  if (!aligned(out, 4)) return DEC_E_ALIGN;
+  const hipError_t e = dec::uniforms_launch(seed, step0, B, n_cb, n_steps * B * n_cb, out,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DEC_OK : hip_fail(e);
+}
+
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream) {
   if (B < 1) return DEC_E_SHAPE;
   if (len == nullptr && step == nullptr) return DEC_E_NULL;

@@ -229,6 +229,14 @@ __device__ __forceinline__ uint64_t philox4x64_10_w0(uint64_t c0, uint64_t c1, u
   return c0;
 }
 
+// The uniform of row (b, c) at step st: counter (st, b, c, 0), key (seed, 0), the top 24
+// bits of word 0 scaled by 2^-24 (exact in float32, in [0, 1)).
+__device__ __forceinline__ float philox_uniform(int st, int b, int c, uint64_t seed) {
+  const uint64_t w = philox4x64_10_w0((uint64_t)(int64_t)st, (uint64_t)b, (uint64_t)c, 0ull, seed,
+                                      0ull);
+  return (float)(uint32_t)(w >> 40) * 0x1p-24f;
+}
+
 __device__ __forceinline__ float logit_at(const float* x, int i) { return x[i]; }
 __device__ __forceinline__ float logit_at(const uint16_t* x, int i) {
   return __uint_as_float(static_cast<uint32_t>(x[i]) << 16);
@@ -337,14 +345,7 @@ __global__ __launch_bounds__(kSampWaves * kWave) void sample_topk_kernel(SampleP
     if (c == 0 && p.len_inc != nullptr) p.len_inc[b] += 1;  // nothing here reads len
   }
   const int started = p.step != nullptr ? (st >= c) : 1;
-  float u;
-  if (p.rng) {  // counter (step, b, c, 0), key (seed, 0): top 24 bits of word 0
-    const uint64_t w = philox4x64_10_w0((uint64_t)(int64_t)st, (uint64_t)b, (uint64_t)c, 0ull,
-                                        p.seed, 0ull);
-    u = (float)(uint32_t)(w >> 40) * 0x1p-24f;
-  } else {
-    u = p.uniforms[row];
-  }
+  const float u = p.rng ? philox_uniform(st, b, c, p.seed) : p.uniforms[row];
 
   // Slots below samp_full_slots(VPL) hold valid entries on every lane (the launcher picks VPL
   // only for rows longer than that many slots), so they load at fixed offsets from one base,
@@ -590,6 +591,23 @@ hipError_t append_launch(const AppendParams& p, hipStream_t stream) {
   long long blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+__global__ void uniforms_kernel(uint64_t seed, int step0, int B, int n_cb, int total, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int rows = B * n_cb;
+  const int s = i / rows;
+  const int row = i - s * rows;
+  const int b = row / n_cb;
+  out[i] = philox_uniform(step0 + s, b, row - b * n_cb, seed);
+}
+
+hipError_t uniforms_launch(uint64_t seed, int step0, int B, int n_cb, int total, float* out,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(uniforms_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     seed, step0, B, n_cb, total, out);
   return hipGetLastError();
 }
 

@@ -142,6 +142,8 @@ _API = {
     "dec_embed_sum": "tokens:i32[B,n_cb] E:bf16[n_cb,V_emb,D] x:f32[B,D] B:int n_cb:int "
                      "V_emb:int D:int stream:stream?",
     "dec_step_advance": "len:i32[B] step:i32[B] B:int stream:stream?",
+    "dec_philox_uniforms": "seed:u64 step0:int n_steps:int B:int n_cb:int "
+                           "out:f32[n_steps,B,n_cb] stream:stream?",
     "dec_probe_read": "buf:bytes[bytes] bytes:size sink:u32[1] stream:stream?",
     "dec_probe_empty": "stream:stream?",
     "dec_probe_clock": "clocks:i64[16] stream:stream?",

@@ -75,6 +75,10 @@ def parse(argv=None):
     ap.add_argument("--decode-loop", action="store_true",
                     help="a workload with a step count (long_output): the whole generation,\n"
                          "lengths and steps advanced on the device, timed end to end")
+    ap.add_argument("--draw-in-sampler", action="store_true",
+                    help="with --decode-loop: each sampler launch draws its own uniforms "
+                         "(Philox in the launch) instead of reading them from one "
+                         "dec_philox_uniforms launch at the start of the generation")
     ap.add_argument("--separate-append", action="store_true",
                     help="with --decode-loop: append the current token's rows with\n"
                          "dec_kv_append as a node of its own (for comparison)")
@@ -170,9 +174,12 @@ def decode_loop(a):
     len_d = d["len"]
     step_d = torch.zeros((B, w.n_codebooks), dtype=torch.int32, device=dev)  # one per row
     seed = 0x5EED_0000_0000_0004
+    # the generation's uniforms, drawn in one launch at its start: step s reads block s
+    # (the same values the sampler would draw at step s)
+    table = torch.empty((S, B, w.n_codebooks), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
 
-    def step(st, s):
+    def step(st, s, i):
         if a.separate_append:
             dec.dec_kv_append(k_new, v_new, st["k_self"], st["v_self"], len_d, w.n_layers, B,
                               w.heads, w.self_cap, w.head_dim, code, s)
@@ -187,7 +194,8 @@ def decode_loop(a):
                                      o_c, w.n_layers, B, w.heads, w.head_dim, code, w.scale,
                                      ws, nb, s)
         dec.dec_sample_topk_advance(d["logits"], dec.DEC_F32, B, w.n_codebooks, w.vocab_valid,
-                                    w.vocab_stride, d["temperature"], w.top_k, None, seed,
+                                    w.vocab_stride, d["temperature"], w.top_k,
+                                    None if a.draw_in_sampler else table[i], seed,
                                     step_d, len_d, w.fill_token, tok, None, None, s)
 
     def reset():
@@ -197,8 +205,10 @@ def decode_loop(a):
     with torch.cuda.stream(stream):
         dec.dec_attn_workspace_init(ws, nb, stream)
         dec.dec_graph_begin(stream)             # the whole generation as one graph
+        if not a.draw_in_sampler:
+            dec.dec_philox_uniforms(seed, 0, S, B, w.n_codebooks, table, stream)
         for s in range(S):
-            step(sets[s % R], stream)
+            step(sets[s % R], stream, s)
         graph = dec.dec_graph_end(stream)
         reset()
         dec.dec_graph_launch(graph, stream)     # one untimed generation
@@ -240,7 +250,12 @@ def decode_loop(a):
                                 f"the current token's rows appended and attended in one "
                                 f"launch; dec_sample_topk_advance: sampling and the length "
                                 f"and step advance in one launch; the steps on {R} cache "
-                                f"sets in turn)")},
+                                f"sets in turn)"),
+                   "uniforms": ("drawn by each sampler launch (Philox4x64-10 in the launch)"
+                                if a.draw_in_sampler else
+                                f"the generation's {S} x {B} x {w.n_codebooks} Philox4x64-10 "
+                                f"uniforms drawn in one dec_philox_uniforms launch at its "
+                                f"start (inside the timed graph); step s reads block s")},
         "total_ms": round(total_ms, 3),
         "total_ms_at_70pct_of_peak": round(total_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 3),
         "roofline": {"bound": "hbm", "kernel": "whole step (append + attention, sampler + advance)",

@@ -401,6 +401,23 @@ int dec_embed_sum(const int32_t* tokens, const void* E, float* x, int B, int n_c
  * len[b] += 1 (if len != NULL) and step[b] += 1 (if step != NULL) for b < B. */
 int dec_step_advance(int32_t* len, int32_t* step, int B, dec_stream_t stream);
 
+/* The uniforms of a run of decode steps, drawn in one launch ahead of them
+ * ("Analysis and improvements": sampling without a GPU/CPU synchronisation; with
+ * the random numbers drawn on the device no step needs host input).  A sampler
+ * launch then reads its step's uniforms (the `uniforms` argument of
+ * dec_sample_topk, _ex or _advance) instead of drawing them in its own launch,
+ * where the ten dependent Philox rounds lengthen the row's critical path.
+ *   out   [n_steps, B, n_cb] float32, 4-byte aligned (DEC_E_ALIGN): out[s, b, c]
+ *         = the uniform of row (b, c) at step step0 + s, exactly the value
+ *         dec_sample_topk_philox draws for that row when step[b] = step0 + s
+ *         (Philox4x64-10, counter (step0 + s, b, c, 0), key (seed, 0), the top
+ *         24 bits of output word 0 times 2^-24)
+ * n_steps, B, n_cb >= 1, step0 >= 0, step0 + n_steps and n_steps * B * n_cb
+ * below 2^31 (else DEC_E_SHAPE); out NULL: DEC_E_NULL.  Device pointer,
+ * caller-owned; nothing else is read or written. */
+int dec_philox_uniforms(uint64_t seed, int step0, int n_steps, int B, int n_cb, float* out,
+                        dec_stream_t stream);
+
 /* Calibration for the measurements; neither is a step of a decode step.
  * dec_probe_read streams [buf, buf + bytes) once (16-byte non-temporal loads,
  * 8 KiB per wavefront, one workgroup of four wavefronts per 32 KiB), giving

@@ -383,6 +383,13 @@ def test_misc_validation():
     assert D.raw_status("dec_probe_read", A, 24, A, None) == D.DEC_E_SHAPE
     assert D.raw_status("dec_probe_read", A + 4, 16, A, None) == D.DEC_E_ALIGN
     assert D.raw_status("dec_probe_read", A, 16, A + 2, None) == D.DEC_E_ALIGN
+    # batch uniforms: a buffer, positive counts, a non-negative first step, 31-bit totals
+    U = "dec_philox_uniforms"
+    assert D.raw_status(U, 7, 0, 4, 1, 9, None, None) == D.DEC_E_NULL
+    for bad in ((7, -1, 4, 1, 9), (7, 0, 0, 1, 9), (7, 0, 4, 0, 9), (7, 0, 4, 1, 0),
+                (7, 0x7FFFFFF0, 100, 1, 9), (7, 0, 1 << 20, 1 << 10, 9)):
+        assert D.raw_status(U, *bad, A, None) == D.DEC_E_SHAPE, bad
+    assert D.raw_status(U, 7, 0, 4, 1, 9, A + 2, None) == D.DEC_E_ALIGN
 
 
 def test_tuning_overrides_round_trip_refuse_out_of_range_and_reset():
@@ -530,7 +537,7 @@ def test_binding_declarations_follow_the_header():
 
 _SIZES = dict(n_layers=2, B=3, H=2, L_cap=5, hd=64, L_cap_self=7, L_cap_cross=6, n_cb=4,
               V_valid=40, V_stride=48, top_k=3, mask_words=2, n_blocks=3, block_size=64,
-              max_blocks=2, D=16, V_emb=9, bytes=64, ws_bytes=256)
+              max_blocks=2, D=16, V_emb=9, bytes=64, ws_bytes=256, n_steps=3)
 
 
 def _good_call(params):

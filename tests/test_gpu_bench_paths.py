@@ -26,6 +26,8 @@ CASES = {
     "eager": ["--eager"],
     "heads": ["--heads"],
     "decode_loop": ["--workload", "long_output", "--decode-loop"],
+    "decode_loop_draw_in_sampler": ["--workload", "long_output", "--decode-loop",
+                                    "--draw-in-sampler"],
     "calibrate": ["--calibrate"],
 }
 SMALL = ["--steps", "4", "--warmup", "1", "--sets", "2", "--kernel-launches", "10",

@@ -8,7 +8,9 @@
   replayed several times with no host input, each replay checked against the oracle, with
   the advance as its own node or inside the sampler (dec_sample_topk_advance);
 * dec_sample_topk_advance equals dec_sample_topk_ex at the counters' step bit for bit, on
-  the narrow and the wide path, and leaves every counter and length one larger.
+  the narrow and the wide path, and leaves every counter and length one larger;
+* dec_philox_uniforms draws the oracle's uniforms for a run of steps in one launch, and a
+  sampler handed them samples exactly what the sampler drawing its own samples.
 """
 import dataclasses
 
@@ -287,3 +289,49 @@ def test_appending_records_over_growing_lengths(tune):
             outs.append([_bits(o_s), _bits(o_c), _bits(r["k"]), _bits(r["v"])])
         for a, b in zip(*outs):
             assert np.array_equal(a, b), (s, lens.tolist())
+
+
+@pytest.mark.parametrize("seed,step0,n_steps,B,n_cb",
+                         [(0x0123_4567_89AB_CDEF, 0, 64, 1, 9), (5, 2040, 8, 33, 9),
+                          (0xFFFF_FFFF_FFFF_FFFF, 123456, 3, 4, 2), (0, 0, 1, 1, 1)])
+def test_batch_uniforms_match_oracle(seed, step0, n_steps, B, n_cb):
+    # dec_philox_uniforms: every step's [B, n_cb] block equals the oracle's Philox4x64-10
+    # uniforms at that step, bit for bit
+    print(f"[uniforms] seed={seed:#x} step0={step0} n_steps={n_steps} B={B} n_cb={n_cb}",
+          flush=True)
+    out = torch.full((n_steps, B, n_cb), -1.0, dtype=torch.float32, device=hp.DEV)
+    dec.dec_philox_uniforms(seed, step0, n_steps, B, n_cb, out)
+    got = hp.host(out)
+    for s in range(n_steps):
+        want = orng.sample_uniforms(seed, np.full(B, step0 + s), n_cb)
+        assert np.array_equal(got[s].view(np.uint32), want.view(np.uint32)), f"step {step0 + s}"
+
+
+@pytest.mark.parametrize("k", [50, 250])
+def test_sampler_reading_batch_uniforms_equals_drawing_them(k):
+    # a generation that draws its uniforms ahead (dec_philox_uniforms) and hands each step
+    # its block samples exactly what the sampler drawing its own (uniforms NULL) samples:
+    # 12 steps from step 5, every output bit for bit
+    B, n_cb, V, S, seed, st0 = 3, 9, 1089, 1096, 0x5EED_0000_0000_0004, 5
+    rng = np.random.default_rng(31 + k)
+    lg = np.full((B, n_cb, S), 1e30, np.float32)
+    lg[:, :, :V] = rng.standard_normal((B, n_cb, V), dtype=np.float32) * 3
+    lg_d, T_d = _dev(lg), _dev(np.array([1.0, 0.7, 1.3], np.float32))
+    print(f"[batch uniforms] k={k}", flush=True)
+    table = torch.empty((12, B, n_cb), dtype=torch.float32, device=hp.DEV)
+    dec.dec_philox_uniforms(seed, st0, 12, B, n_cb, table)
+    step_a = _dev(np.full((B, n_cb), st0, np.int32))
+    step_b = _dev(np.full((B, n_cb), st0, np.int32))
+    mk = lambda: [torch.zeros((B, n_cb), dtype=torch.int32, device=hp.DEV),
+                  torch.zeros((B, n_cb, k), dtype=torch.int32, device=hp.DEV),
+                  torch.zeros((B, n_cb, k), dtype=torch.float32, device=hp.DEV)]
+    drawn, read = mk(), mk()
+    for i in range(12):
+        dec.dec_sample_topk_advance(lg_d, dec.DEC_F32, B, n_cb, V, S, T_d, k, None, seed,
+                                    step_a, None, 1089, *drawn)
+        dec.dec_sample_topk_advance(lg_d, dec.DEC_F32, B, n_cb, V, S, T_d, k, table[i], seed,
+                                    step_b, None, 1089, *read)
+        torch.cuda.synchronize()
+        for a, r in zip(drawn, read):
+            assert np.array_equal(_bits(a), _bits(r)), f"step {st0 + i}"
+    assert np.array_equal(hp.host(step_a), hp.host(step_b))
